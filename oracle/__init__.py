@@ -1,0 +1,179 @@
+"""CPU oracle for quantized-KV attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package.  The GPU library (``decode_attention_group_amd``)
+never imports, loads or calls it, and the two share no code.
+
+The arithmetic lives in ``kvq_oracle.c`` (fp32 quantizer, fp64 dequantization
+and attention); this module builds it with gcc and wraps it with ctypes over
+numpy arrays.  Citations refer to pages 78, 80 and 81 of the
+@mlx-bun/inference 0.0.0-stage -> 1.0.0 diff on my.diffend.io.
+
+Layouts here are the plain ones:
+  codes   uint8  [B][H][R][D]         one code per byte
+  scales  uint16 [B][H][R][D/64]      bf16 bit patterns
+  biases  uint16 [B][H][R][D/64]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB = os.path.join(_HERE, "libkvq_oracle.so")
+GROUP = 64
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    """A non-zero status from the oracle (1: invalid argument, 2: capacity)."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: oracle status {status}")
+        self.status = status
+
+
+def build(force: bool = True) -> str:
+    """Compile kvq_oracle.c with gcc (IEEE fp32, no contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+            _SRC, "-o", tmp, "-lm",
+        ])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        lib.kvqo_quantize_group.argtypes = [P, i32, i32, P, P, P]
+        lib.kvqo_quantize_group.restype = i32
+        lib.kvqo_append.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P, P]
+        lib.kvqo_append.restype = i32
+        lib.kvqo_pack_words.argtypes = [P, ctypes.c_int64, i32, i32, P]
+        lib.kvqo_pack_words.restype = None
+        lib.kvqo_dequant.argtypes = [P, P, P, ctypes.c_int64, i32, P]
+        lib.kvqo_dequant.restype = None
+        lib.kvqo_attend.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                    P, i32, i32, P, ctypes.c_double, P, i32]
+        lib.kvqo_attend.restype = i32
+        lib.kvqo_max_threads.argtypes = []
+        lib.kvqo_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().kvqo_max_threads())
+
+
+def quantize_group(x, bits: int):
+    """Quantize one group (any length, normally 64) -> (codes uint8, scale_bits, bias_bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.zeros(x.size, np.uint8)
+    s = np.zeros(1, np.uint16)
+    b = np.zeros(1, np.uint16)
+    st = _load().kvqo_quantize_group(_ptr(x), x.size, bits, _ptr(codes), _ptr(s), _ptr(b))
+    if st:
+        raise OracleError(st, "quantize_group")
+    return codes, int(s[0]), int(b[0])
+
+
+class Cache:
+    """A plain-layout quantized cache for one layer (K and V, each with its own width)."""
+
+    def __init__(self, B: int, H: int, D: int, R: int, k_bits: int, v_bits: int, window: int = 0):
+        if D % GROUP:
+            raise ValueError("head_dim must be a multiple of 64")
+        self.B, self.H, self.D, self.R = B, H, D, R
+        self.k_bits, self.v_bits, self.window = k_bits, v_bits, window
+        G = D // GROUP
+        self.k_codes = np.zeros((B, H, R, D), np.uint8)
+        self.v_codes = np.zeros((B, H, R, D), np.uint8)
+        self.k_scales = np.zeros((B, H, R, G), np.uint16)
+        self.k_biases = np.zeros((B, H, R, G), np.uint16)
+        self.v_scales = np.zeros((B, H, R, G), np.uint16)
+        self.v_biases = np.zeros((B, H, R, G), np.uint16)
+
+    def append(self, k, v, pos0):
+        """Quantize-and-append T tokens: k, v fp32 [B][H][T][D]; pos0 [B]."""
+        k = np.ascontiguousarray(k, dtype=np.float32)
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        pos0 = np.ascontiguousarray(pos0, dtype=np.int32)
+        B, H, T, D = k.shape
+        assert (B, H, D) == (self.B, self.H, self.D) and v.shape == k.shape
+        lib = _load()
+        for x, bits, c, s, b, what in ((k, self.k_bits, self.k_codes, self.k_scales, self.k_biases, "K"),
+                                       (v, self.v_bits, self.v_codes, self.v_scales, self.v_biases, "V")):
+            st = lib.kvqo_append(_ptr(x), B, H, T, D, bits, self.R, _ptr(pos0), _ptr(c), _ptr(s), _ptr(b))
+            if st:
+                raise OracleError(st, f"append {what}")
+
+    def packed_k(self):
+        """K codes packed per row into uint32 words, [B][H][R][D*bits/32]."""
+        return pack_words(self.k_codes, self.k_bits)
+
+    def dequant_k(self):
+        return dequant(self.k_codes, self.k_scales, self.k_biases)
+
+    def dequant_v(self):
+        return dequant(self.v_codes, self.v_scales, self.v_biases)
+
+    def attend(self, q_bits, len_, scale: float = 1.0, nthreads: int = 0):
+        """fp64 attention of q (bf16 bit patterns, [B][Hq][C][D]) over this cache."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        len_ = np.ascontiguousarray(len_, dtype=np.int32)
+        B, Hq, C, D = q_bits.shape
+        assert B == self.B and D == self.D
+        out = np.zeros((B, Hq, C, D), np.float64)
+        st = _load().kvqo_attend(
+            _ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.k_biases),
+            _ptr(self.v_codes), _ptr(self.v_scales), _ptr(self.v_biases),
+            B, self.H, D, self.R, self.window, _ptr(q_bits), Hq, C, _ptr(len_),
+            float(scale), _ptr(out), int(nthreads))
+        if st:
+            raise OracleError(st, "attend")
+        return out
+
+
+def pack_words(codes, bits: int):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    D = codes.shape[-1]
+    rows = codes.size // D
+    out = np.zeros(codes.shape[:-1] + (D * bits // 32,), np.uint32)
+    _load().kvqo_pack_words(_ptr(codes), rows, D, bits, _ptr(out))
+    return out
+
+
+def dequant(codes, scales, biases):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    biases = np.ascontiguousarray(biases, dtype=np.uint16)
+    D = codes.shape[-1]
+    out = np.zeros(codes.shape, np.float64)
+    _load().kvqo_dequant(_ptr(codes), _ptr(scales), _ptr(biases), codes.size // D, D, _ptr(out))
+    return out
+
+
+def attend_shared(cache: Cache, q_layers, len_, scale: float = 1.0, nthreads: int = 0):
+    """Several KV-sharing layers reading one donor cache [p80 model.ts header: KV-shared
+    layers; p78 gemma4-e4b.ts Gemma4Layer.cache]: each layer's queries attend the same
+    cache with the donor's positions and window, i.e. one attend() per layer."""
+    return [cache.attend(q, len_, scale, nthreads) for q in q_layers]
