@@ -1,0 +1,168 @@
+// Quantize-and-append: fp32 keys/values -> affine group-64 codes written at
+// ring slots (page 80 of the @mlx-bun/inference 0.0.0-stage -> 1.0.0 diff,
+// model.ts attentionTraining: cache.appendWindow before the read; page 78,
+// gemma4-e4b.ts Gemma4Layer.kv: 4- or 8-bit affine codes, group 64).
+//
+// One workgroup owns one 8-slot block of one (sequence, KV head) cache, for K
+// or for V, so the blocked V words of that block are read-merged-written by a
+// single workgroup: no two workgroups of a call touch the same word.
+// Eight consecutive lanes quantize one 64-value group (8 values each); the
+// group's min and max meet through three butterfly shuffles.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+#pragma clang fp contract(off)
+
+// Largest bf16 value <= x (x finite): clearing the low 16 bits moves toward
+// zero, which is downward only for x >= 0; a negative x steps one bf16 unit
+// further from zero instead.
+__device__ __forceinline__ float bf16_round_down(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0xFFFFu) == 0u) return x;
+    const uint32_t t = u & 0xFFFF0000u;
+    return __uint_as_float((u & 0x80000000u) ? t + 0x10000u : t);
+}
+
+// Smallest bf16 value >= x (x finite, here always >= 0).
+__device__ __forceinline__ float bf16_round_up(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0xFFFFu) == 0u) return x;
+    const uint32_t t = u & 0xFFFF0000u;
+    return __uint_as_float((u & 0x80000000u) ? t : t + 0x10000u);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p)
+{
+    constexpr int G = D / 64;
+    constexpr int CH = D / 8;                 // 8-value chunks per slot
+    __shared__ int tok[8];                    // token written into each slot of the block, or -1
+    __shared__ uint8_t vcode[8][D];           // V codes of the block, slot-major
+
+    const int b = blockIdx.z >> 1;
+    const bool is_v = blockIdx.z & 1;
+    const int h = blockIdx.y;
+    const int H = p.H, R = p.R, T = p.T;
+    const int bits = is_v ? p.v_bits : p.k_bits;
+    const float* __restrict__ x = is_v ? p.v : p.k;
+    uint32_t* __restrict__ codes = is_v ? p.v_codes : p.k_codes;
+    uint32_t* __restrict__ sb = is_v ? p.v_sb : p.k_sb;
+    const int nblk = R / 8;
+    const int64_t bh = (int64_t)b * H + h;
+
+    const int64_t p_lo = (int64_t)p.pos0[b] + p.t_first;
+    const int first_slot = (int)(((p_lo % R) + R) % R);   // in [0, R) even for a bad pos0
+    const int blk = (first_slot / 8 + (int)blockIdx.x) % nblk;
+    if (threadIdx.x < 8) {
+        const int slot = blk * 8 + threadIdx.x;
+        const int off = (slot - first_slot + R) % R;
+        tok[threadIdx.x] = off < p.n_written ? p.t_first + off : -1;
+    }
+    __syncthreads();
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) any |= tok[j] >= 0;
+    if (!any) return;
+
+    const int top = (1 << bits) - 1;
+    for (int task = threadIdx.x; task < 8 * CH; task += blockDim.x) {
+        const int j = task / CH;              // slot within the block
+        const int ch = task % CH;             // values [8*ch, 8*ch + 8)
+        const int t = tok[j];
+        if (t < 0) continue;                  // whole 8-lane groups skip together
+        const float* src = x + ((bh * T + t) * D + ch * 8);
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 c = *reinterpret_cast<const float4*>(src + 4);
+        float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        mn = mn + 0.0f;                       // -0 reads as +0
+        mx = mx + 0.0f;
+        const float bias = bf16_round_down(mn);
+        const float step = (mx - bias) / (float)top;
+        const float scale = bf16_round_up(step);
+        uint32_t q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float r = 0.0f;
+            if (scale != 0.0f) {
+                r = __builtin_rintf((v[e] - bias) / scale);
+                r = fminf(fmaxf(r, 0.0f), (float)top);
+            }
+            q[e] = (uint32_t)r;
+        }
+        const int slot = blk * 8 + j;
+        if ((ch & 7) == 0)
+            sb[(bh * R + slot) * G + (ch >> 3)] =
+                (__float_as_uint(scale) >> 16) | (__float_as_uint(bias) & 0xFFFF0000u);
+        if (!is_v) {
+            uint32_t* row = codes + (bh * R + slot) * (int64_t)(D * bits / 32);
+            if (bits == 8) {
+                uint2 w;
+                w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+                w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+                *reinterpret_cast<uint2*>(row + ch * 2) = w;
+            } else {
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w |= q[e] << (4 * e);
+                row[ch] = w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vcode[j][ch * 8 + e] = (uint8_t)q[e];
+        }
+    }
+    if (!is_v) return;
+    __syncthreads();
+
+    // Merge the block's new V codes into its words: for each d, the 8 slots'
+    // codes sit in bits/4 words, slot t at bits [bits*t, bits*(t+1)).
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) all &= tok[j] >= 0;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        uint32_t* w = codes + ((bh * nblk + blk) * D + d) * (bits / 4);
+        if (bits == 4) {
+            uint32_t acc = all ? 0u : w[0];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (tok[j] >= 0) acc = (acc & ~(0xFu << (4 * j))) | ((uint32_t)vcode[j][d] << (4 * j));
+            w[0] = acc;
+        } else {
+            uint32_t lo = all ? 0u : w[0], hi = all ? 0u : w[1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (tok[j] >= 0) lo = (lo & ~(0xFFu << (8 * j))) | ((uint32_t)vcode[j][d] << (8 * j));
+#pragma unroll
+            for (int j = 4; j < 8; ++j)
+                if (tok[j] >= 0) hi = (hi & ~(0xFFu << (8 * (j - 4)))) | ((uint32_t)vcode[j][d] << (8 * (j - 4)));
+            w[0] = lo;
+            w[1] = hi;
+        }
+    }
+}
+
+hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream)
+{
+    const dim3 grid(n_cand, p.H, 2 * p.B);
+    switch (p.D) {
+    case 128: append_kernel<128><<<grid, 256, 0, stream>>>(p); break;
+    case 256: append_kernel<256><<<grid, 256, 0, stream>>>(p); break;
+    case 512: append_kernel<512><<<grid, 256, 0, stream>>>(p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,354 @@
+// Host side of the C ABI declared in include/kvq.h: argument validation, launch
+// planning (row tiles, split-KV), workspace sizing and thread-local errors.
+// Nothing here allocates device memory.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+#define KVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvq_status ok()
+{
+    g_err[0] = '\0';
+    return KVQ_OK;
+}
+
+bool trace_on()
+{
+    static const int on = [] { const char* e = getenv("KVQ_TRACE"); return e && *e && *e != '0'; }();
+    return on != 0;
+}
+
+kvq_status check_cache(const kvq_cache* c, const char* what)
+{
+    if (!c) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: cache descriptor is NULL", what);
+    if (!c->k_codes || !c->v_codes || !c->k_sb || !c->v_sb)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: a cache array pointer is NULL", what);
+    if (c->group_size != KVQ_GROUP_SIZE)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (only 64 is supported)", what, c->group_size);
+    if (c->head_dim != 128 && c->head_dim != 256 && c->head_dim != 512)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256, 512)", what, c->head_dim);
+    if ((c->k_bits != 4 && c->k_bits != 8) || (c->v_bits != 4 && c->v_bits != 8))
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: k_bits %d / v_bits %d (each must be 4 or 8)", what, c->k_bits, c->v_bits);
+    if (c->batch < 1 || c->n_kv_heads < 1)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d and n_kv_heads %d must be >= 1", what, c->batch, c->n_kv_heads);
+    if (c->capacity < KVQ_V_BLOCK || c->capacity % KVQ_V_BLOCK != 0)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d must be a positive multiple of 8", what, c->capacity);
+    if (c->window < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: window %d < 0", what, c->window);
+    if (c->window > c->capacity)
+        return fail(KVQ_ERR_CAPACITY, "%s: window %d exceeds capacity %d", what, c->window, c->capacity);
+    if (c->capacity > (INT_MAX / 2))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d too large", what, c->capacity);
+    return KVQ_OK;
+}
+
+int env_splits()
+{
+    const char* e = getenv("KVQ_SPLITS");
+    return e ? atoi(e) : 0;
+}
+
+// One read of one cache by `n_layers` layers (decode/shared) or by a chunk of
+// C queries (prefill).
+struct ReadSpec {
+    const kvq_cache* cache;
+    int n_layers;
+    const uint16_t* const* q;
+    uint16_t* const* out;
+    int Hq;
+    float scale;
+    const int32_t* len;
+    int max_len;
+    int C;             // 1: decode rows are layers x heads; > 1: prefill rows are queries x heads
+};
+
+kvq_status check_read(const ReadSpec& r, const char* what)
+{
+    kvq_status st = check_cache(r.cache, what);
+    if (st != KVQ_OK) return st;
+    const kvq_cache* c = r.cache;
+    if (r.n_layers < 1 || r.n_layers > KVQ_MAX_SHARED_LAYERS)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_layers %d outside [1, %d]", what, r.n_layers, KVQ_MAX_SHARED_LAYERS);
+    if (!r.q || !r.out) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q/out pointer array is NULL", what);
+    for (int l = 0; l < r.n_layers; ++l)
+        if (!r.q[l] || !r.out[l]) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q or out of layer %d is NULL", what, l);
+    if (!r.len) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: len is NULL", what);
+    if (r.Hq < 1 || r.Hq % c->n_kv_heads != 0)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_q_heads %d is not a positive multiple of n_kv_heads %d",
+                    what, r.Hq, c->n_kv_heads);
+    if (!std::isfinite(r.scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: scale is not finite", what);
+    if (r.C < 1) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: chunk %d < 1", what, r.C);
+    if (r.max_len < r.C)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: max_len %d < %d queries per sequence", what, r.max_len, r.C);
+    if (c->window == 0 && r.max_len > c->capacity)
+        return fail(KVQ_ERR_CAPACITY, "%s: full-attention cache of capacity %d cannot hold max_len %d",
+                    what, c->capacity, r.max_len);
+    if (c->window > 0 && (int64_t)c->window + r.C - 1 > c->capacity)
+        return fail(KVQ_ERR_CAPACITY, "%s: window %d + chunk %d - 1 exceeds capacity %d",
+                    what, c->window, r.C, c->capacity);
+    const int64_t rows = (int64_t)(r.C == 1 ? r.n_layers : r.C) * (r.Hq / c->n_kv_heads);
+    if (rows > (1 << 24)) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: too many query rows", what);
+    return KVQ_OK;
+}
+
+// Fill the descriptor's shape and split plan.  `target_wg` is the number of
+// workgroups this read should aim for.
+void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
+{
+    const kvq_cache* c = r.cache;
+    std::memset(&d, 0, sizeof(d));
+    d.k_codes = c->k_codes;
+    d.v_codes = c->v_codes;
+    d.k_sb = c->k_sb;
+    d.v_sb = c->v_sb;
+    for (int l = 0; l < r.n_layers && l < KVQ_MAX_SHARED_LAYERS; ++l) {   // sizing queries pass no pointers
+        d.q[l] = r.q ? r.q[l] : nullptr;
+        d.out[l] = r.out ? r.out[l] : nullptr;
+    }
+    d.len = r.len;
+    d.B = c->batch;
+    d.Hkv = c->n_kv_heads;
+    d.Hq = r.Hq;
+    d.R = c->capacity;
+    d.W = c->window;
+    d.C = r.C;
+    d.D = c->head_dim;
+    d.max_len = r.max_len;
+    d.hpk = r.Hq / c->n_kv_heads;
+    d.n_rows = (r.C == 1 ? r.n_layers : r.C) * d.hpk;
+    d.n_rt = (d.n_rows + kvq::kRowTile - 1) / kvq::kRowTile;
+    d.scale_log2e = r.scale * kvq::kLog2e;
+    d.cfg = kvq::cfg_id(c->head_dim, c->k_bits, c->v_bits);
+
+    // Keys one row tile can see, plus the alignment of its first step.
+    int64_t vis = r.max_len;
+    if (c->window > 0) {
+        const int64_t span = r.C == 1 ? 1 : (kvq::kRowTile + d.hpk - 1) / d.hpk + 1;
+        vis = std::min<int64_t>(vis, (int64_t)c->window + span);
+    }
+    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
+    const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
+    int64_t S = (target_wg + items - 1) / items;
+    const int64_t min_steps_per_split = 8;          // two steps per wave
+    S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
+    const int forced = env_splits();
+    if (forced > 0) S = forced;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
+    const int64_t steps_per = (steps + S - 1) / S;
+    d.split_len = (int)(steps_per * kvq::kStep);
+    d.S = (int)((steps + steps_per - 1) / steps_per);
+    d.n_items = (int)(items * d.S);
+}
+
+size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
+{
+    std::memset(&P, 0, sizeof(P));
+    P.n_desc = n;
+    double bytes[KVQ_MAX_SHARED_GROUPS];
+    double total = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const kvq_cache* c = rs[i].cache;
+        const double per_key = c->head_dim * (c->k_bits + c->v_bits) / 8.0 + 4.0 * 2 * c->head_dim / 64;
+        const double vis = c->window > 0 ? std::min(c->window, rs[i].max_len) : rs[i].max_len;
+        bytes[i] = (double)c->batch * c->n_kv_heads * vis * per_key;
+        total += bytes[i];
+    }
+    const int kTargetWg = 512;   // two 4-wave workgroups per CU on 256 CUs
+    total_items = 0;
+    int comb = 0;
+    size_t ws = 0;
+    for (int i = 0; i < n; ++i) {
+        const int target = std::max(1, (int)std::lround(kTargetWg * (total > 0 ? bytes[i] / total : 1.0)));
+        plan_read(rs[i], target, P.d[i]);
+        P.d[i].item_begin = total_items;
+        total_items += P.d[i].n_items;
+        P.d[i].comb_begin = comb;
+        if (P.d[i].S > 1) comb += P.d[i].B * P.d[i].Hkv * P.d[i].n_rt;
+        const size_t f = kvq::part_floats(P.d[i]);
+        ws = (ws + 255) & ~(size_t)255;
+        if (f) ws += f * sizeof(float);
+    }
+    return ws;
+}
+
+void bind_workspace(kvq::AttnParams& P, void* workspace)
+{
+    size_t off = 0;
+    for (int i = 0; i < P.n_desc; ++i) {
+        const size_t f = kvq::part_floats(P.d[i]);
+        off = (off + 255) & ~(size_t)255;
+        P.d[i].part = f ? reinterpret_cast<float*>(static_cast<char*>(workspace) + off) : nullptr;
+        off += f * sizeof(float);
+    }
+}
+
+kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, const char* what)
+{
+    kvq::AttnParams P;
+    int total_items = 0;
+    const size_t need = plan_all(rs, n, P, total_items);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
+    bind_workspace(P, workspace);
+    bool same = true, big = true;
+    for (int i = 0; i < n; ++i) {
+        same &= P.d[i].cfg == P.d[0].cfg;
+        big &= P.d[i].D >= 256;
+    }
+    if (trace_on())
+        for (int i = 0; i < n; ++i)
+            fprintf(stderr, "[kvq] %s desc %d: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d tiles=%d S=%d split=%d wg=%d\n",
+                    what, i, P.d[i].B, P.d[i].Hkv, P.d[i].Hq, P.d[i].D, P.d[i].R, P.d[i].W, P.d[i].C,
+                    P.d[i].n_rows, P.d[i].n_rt, P.d[i].S, P.d[i].split_len, P.d[i].n_items);
+    hipError_t e = hipSuccess;
+    if (same || big) {
+        e = kvq::launch_attn(P, total_items, !same, stream);
+    } else {
+        // Mixed configurations outside the fused set: one launch per descriptor.
+        for (int i = 0; i < n && e == hipSuccess; ++i) {
+            kvq::AttnParams one;
+            std::memset(&one, 0, sizeof(one));
+            one.n_desc = 1;
+            one.d[0] = P.d[i];
+            one.d[0].item_begin = 0;
+            e = kvq::launch_attn(one, P.d[i].n_items, false, stream);
+        }
+    }
+    if (e == hipSuccess) e = kvq::launch_combine(P, stream);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+KVQ_API const char* kvq_last_error(void) { return g_err; }
+
+KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, const float* v,
+                                       int32_t T, const int32_t* pos0, hipStream_t stream)
+{
+    const char* what = "kvq_append_quantize";
+    kvq_status st = check_cache(cache, what);
+    if (st != KVQ_OK) return st;
+    if (T < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: T %d < 0", what, T);
+    if (T == 0) return ok();
+    if (!k || !v || !pos0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k, v or pos0 is NULL", what);
+    if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k and v must be 16-byte aligned", what);
+    kvq::AppendParams p;
+    p.k = k;
+    p.v = v;
+    p.k_codes = cache->k_codes;
+    p.v_codes = cache->v_codes;
+    p.k_sb = cache->k_sb;
+    p.v_sb = cache->v_sb;
+    p.pos0 = pos0;
+    p.B = cache->batch;
+    p.H = cache->n_kv_heads;
+    p.T = T;
+    p.D = cache->head_dim;
+    p.R = cache->capacity;
+    p.k_bits = cache->k_bits;
+    p.v_bits = cache->v_bits;
+    p.t_first = T > p.R ? T - p.R : 0;
+    p.n_written = T - p.t_first;
+    const int n_cand = std::min(p.R / 8, (p.n_written + 7) / 8 + 1);
+    if (2 * (int64_t)p.B > 65535) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d too large", what, p.B);
+    if (trace_on())
+        fprintf(stderr, "[kvq] %s: B=%d H=%d T=%d D=%d R=%d bits=%d/%d blocks=%d\n", what, p.B, p.H, T, p.D, p.R,
+                p.k_bits, p.v_bits, n_cand);
+    const hipError_t e = kvq::launch_append(p, n_cand, stream);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_t n_groups)
+{
+    if (!groups || n_groups < 1 || n_groups > KVQ_MAX_SHARED_GROUPS) return SIZE_MAX;
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    for (int i = 0; i < n_groups; ++i) {
+        const kvq_shared_group& g = groups[i];
+        rs[i] = ReadSpec{g.cache, g.n_layers, g.q, g.out, g.n_q_heads, g.scale, g.len, g.max_len, 1};
+        // Pointer arrays are not needed for sizing.
+        if (check_cache(g.cache, "kvq_decode_workspace_bytes") != KVQ_OK) return SIZE_MAX;
+        if (g.n_layers < 1 || g.n_layers > KVQ_MAX_SHARED_LAYERS || g.n_q_heads < 1 ||
+            g.n_q_heads % g.cache->n_kv_heads != 0 || g.max_len < 1)
+            return SIZE_MAX;
+    }
+    kvq::AttnParams P;
+    int total = 0;
+    return plan_all(rs, n_groups, P, total);
+}
+
+KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t chunk, int32_t max_len)
+{
+    if (check_cache(cache, "kvq_prefill_workspace_bytes") != KVQ_OK) return SIZE_MAX;
+    if (n_q_heads < 1 || n_q_heads % cache->n_kv_heads != 0 || chunk < 1 || max_len < chunk) return SIZE_MAX;
+    ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, chunk};
+    kvq::AttnParams P;
+    int total = 0;
+    return plan_all(&r, 1, P, total);
+}
+
+KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
+                                   const int32_t* len, int32_t max_len, float scale, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char* what = "kvq_attn_decode";
+    const uint16_t* qs[1] = {q};
+    uint16_t* os[1] = {out};
+    ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1};
+    kvq_status st = check_read(r, what);
+    if (st != KVQ_OK) return st;
+    return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+}
+
+KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
+                                          int32_t chunk, const int32_t* len, int32_t max_len, float scale,
+                                          uint16_t* out, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream)
+{
+    const char* what = "kvq_attn_prefill_chunk";
+    const uint16_t* qs[1] = {q};
+    uint16_t* os[1] = {out};
+    ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, chunk};
+    kvq_status st = check_read(r, what);
+    if (st != KVQ_OK) return st;
+    return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+}
+
+KVQ_API kvq_status kvq_attn_decode_shared(const kvq_shared_group* groups, int32_t n_groups,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char* what = "kvq_attn_decode_shared";
+    if (!groups) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: groups is NULL", what);
+    if (n_groups < 1 || n_groups > KVQ_MAX_SHARED_GROUPS)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_groups %d outside [1, %d]", what, n_groups, KVQ_MAX_SHARED_GROUPS);
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    for (int i = 0; i < n_groups; ++i) {
+        const kvq_shared_group& g = groups[i];
+        rs[i] = ReadSpec{g.cache, g.n_layers, g.q, g.out, g.n_q_heads, g.scale, g.len, g.max_len, 1};
+        kvq_status st = check_read(rs[i], what);
+        if (st != KVQ_OK) return st;
+    }
+    return run_reads(rs, n_groups, workspace, workspace_bytes, stream, what);
+}

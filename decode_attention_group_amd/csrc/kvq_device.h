@@ -1,0 +1,108 @@
+// Device helpers for the gfx950 kernels: vector types, code -> fp16 conversion,
+// MFMA wrappers and wave-level reductions.  Wave64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp16 pair holding two 8-bit codes exactly.  v_perm_b32 builds the bytes
+// {code_a, 0x64, code_b, 0x64}: the fp16 values 1024 + code, exact because
+// fp16 has a 10-bit fraction; subtracting 1024 leaves the codes themselves.
+// `sel` picks the code bytes: 0x04010400 -> bytes 0,1; 0x04030402 -> bytes 2,3.
+// (v_perm_b32 D = bytes of {src0:src1}; selector 0..3 = src1 bytes, 4..7 = src0.)
+__device__ __forceinline__ f16x2 u8pair_to_f16x2(uint32_t w, uint32_t sel)
+{
+    const uint32_t m = __builtin_amdgcn_perm(0x64646464u, w, sel);
+    f16x2 h = __builtin_bit_cast(f16x2, m);
+    return h - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
+// fp16 pair holding nibbles i and i+4 of w (i in 0..3) exactly, the same way.
+__device__ __forceinline__ f16x2 u4pair_to_f16x2(uint32_t w, int i)
+{
+    const uint32_t m = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    f16x2 h = __builtin_bit_cast(f16x2, m);
+    return h - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
+// 16 8-bit codes (4 words) -> two MFMA operands of 8 fp16 each, in element order.
+__device__ __forceinline__ void codes8x16_to_f16(const u32x4 w, f16x8 &a0, f16x8 &a1)
+{
+    f16x2 p0 = u8pair_to_f16x2(w.x, 0x04010400u), p1 = u8pair_to_f16x2(w.x, 0x04030402u);
+    f16x2 p2 = u8pair_to_f16x2(w.y, 0x04010400u), p3 = u8pair_to_f16x2(w.y, 0x04030402u);
+    f16x2 p4 = u8pair_to_f16x2(w.z, 0x04010400u), p5 = u8pair_to_f16x2(w.z, 0x04030402u);
+    f16x2 p6 = u8pair_to_f16x2(w.w, 0x04010400u), p7 = u8pair_to_f16x2(w.w, 0x04030402u);
+    a0 = (f16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+    a1 = (f16x8){p4.x, p4.y, p5.x, p5.y, p6.x, p6.y, p7.x, p7.y};
+}
+
+// 8 8-bit codes (2 words) -> one operand of 8 fp16, element order.
+__device__ __forceinline__ f16x8 codes8x8_to_f16(const u32x2 w)
+{
+    f16x2 p0 = u8pair_to_f16x2(w.x, 0x04010400u), p1 = u8pair_to_f16x2(w.x, 0x04030402u);
+    f16x2 p2 = u8pair_to_f16x2(w.y, 0x04010400u), p3 = u8pair_to_f16x2(w.y, 0x04030402u);
+    return (f16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// 8 4-bit codes (1 word) -> one operand of 8 fp16 in the element order
+// {0,4,1,5,2,6,3,7} (the order the nibble pairs come out in).
+__device__ __forceinline__ f16x8 codes4x8_to_f16(uint32_t w)
+{
+    f16x2 p0 = u4pair_to_f16x2(w, 0), p1 = u4pair_to_f16x2(w, 1);
+    f16x2 p2 = u4pair_to_f16x2(w, 2), p3 = u4pair_to_f16x2(w, 3);
+    return (f16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Element e of an 8-wide 4-bit operand holds code index kNib[e].
+__device__ __forceinline__ constexpr int nib_order(int e) { return (e & 1) ? 4 + (e >> 1) : (e >> 1); }
+
+// 16x16x32 MFMA, fp16 / bf16 inputs, fp32 accumulate.  Lane l supplies A row
+// (l%16) and B column (l%16) with 8 K-values each; lanes l, l+16, l+32, l+48
+// together cover K = 32.  The result lane l holds C[4*(l/16) + i][l%16], i < 4.
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Reductions across the four 16-lane row groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_across_groups(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum_across_groups(float v)
+{
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace kvq

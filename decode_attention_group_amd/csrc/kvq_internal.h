@@ -1,0 +1,78 @@
+// Launch parameter blocks shared by the host API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+struct AppendParams {
+    const float* k;
+    const float* v;
+    uint32_t* k_codes;
+    uint32_t* v_codes;
+    uint32_t* k_sb;
+    uint32_t* v_sb;
+    const int32_t* pos0;
+    int32_t B, H, T, D, R;
+    int32_t k_bits, v_bits;
+    int32_t t_first;      // first token written (T > R keeps the last R)
+    int32_t n_written;    // tokens written per sequence
+};
+
+// Rows of one (sequence, KV head) pair are the query rows that read it:
+//   decode / shared: row = layer * hpk + h   (hpk = Hq / Hkv query heads per KV head)
+//   prefill:         row = i * hpk + h       (i = query index in the chunk)
+// Rows are processed in tiles of 16; a work item is (b, kv head, row tile, split).
+constexpr int kRowTile = 16;
+constexpr int kStep = 32;          // keys per inner step
+constexpr int kMaxSplits = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnDesc {
+    const uint32_t* k_codes;
+    const uint32_t* v_codes;
+    const uint32_t* k_sb;
+    const uint32_t* v_sb;
+    const uint16_t* q[KVQ_MAX_SHARED_LAYERS];
+    uint16_t* out[KVQ_MAX_SHARED_LAYERS];
+    const int32_t* len;
+    float* part;            // split partials (null when S == 1)
+    int32_t B, Hkv, Hq, R, W, C, D;
+    int32_t max_len;        // len[b] is clamped to [0, max_len]
+    int32_t hpk, n_rows, n_rt;
+    int32_t S, split_len;   // splits per (b, kv head, row tile) and keys per split
+    int32_t item_begin;     // first workgroup of this descriptor
+    int32_t n_items;        // B * Hkv * n_rt * S
+    int32_t comb_begin;     // first combine workgroup of this descriptor (S > 1)
+    float scale_log2e;
+    int32_t cfg;            // kernel configuration id (head_dim, k_bits, v_bits)
+};
+
+struct AttnParams {
+    AttnDesc d[KVQ_MAX_SHARED_GROUPS];
+    int32_t n_desc;
+};
+
+inline int cfg_id(int D, int kb, int vb)
+{
+    const int di = D == 128 ? 0 : D == 256 ? 1 : 2;
+    return di * 4 + (kb == 8 ? 2 : 0) + (vb == 8 ? 1 : 0);
+}
+
+// Partial buffer of one descriptor: o [B*Hkv*n_rt][S][16][D] fp32, then
+// (m, l) [B*Hkv*n_rt][S][16][2] fp32.
+inline size_t part_floats(const AttnDesc& d)
+{
+    if (d.S <= 1) return 0;
+    const size_t items = (size_t)d.B * d.Hkv * d.n_rt * d.S * kRowTile;
+    return items * (size_t)d.D + items * 2;
+}
+
+hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
+hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
+hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,205 @@
+/*
+ * kvq.h -- quantized-KV attention on AMD Instinct MI355X (gfx950).
+ *
+ * Scaled-dot-product attention over a per-layer KV cache held in affine group
+ * quantization (4- or 8-bit codes, 64 values per group along head_dim, one
+ * bf16 scale and one bf16 bias per group), for the decode and chunked-prefill
+ * reads of a Gemma 4 text model.
+ *
+ * What the calls compute comes from the pages of the @mlx-bun/inference
+ * 0.0.0-stage -> 1.0.0 diff on my.diffend.io:
+ *   page 80, gemma4/model.ts, header notes: SDPA scale is 1.0 because q and k are
+ *     RMS-normalised; full-attention layers have head_dim 512 and one KV head;
+ *     sliding layers read a rotating cache whose reads own the window; KV-shared
+ *     layers read a donor layer's cache;
+ *   page 80, gemma4/model.ts, attentionTraining: keys and values are transposed
+ *     to [B, H, L, D], appended to the layer's cache (cache.appendWindow), and
+ *     the queries attend that read (read.attend(q, 1.0)); a sharer with no KV
+ *     projection appends nothing and reads its donor;
+ *   page 80, model.ts, decode / prompt phase declarations: decode is one new
+ *     token per sequence; a prompt chunk is many tokens per sequence;
+ *   page 78, gemma4-e4b.ts, Gemma4Layer and LAYERS: every cache is affine
+ *     quantized with a width of 4 or 8 bits and a group of 64; sharers attend
+ *     the last donor of their own attention type.
+ * The pages give no quantization formula; this library uses, bit for bit:
+ *     bias  = min(group) rounded down to bf16 (-0 read as +0)
+ *     scale = ((max(group) - bias) / (2^bits - 1)) rounded up to bf16
+ *     code  = clamp(rint((x - bias) / scale), 0, 2^bits - 1)   (0 when scale == 0)
+ * with every step a single IEEE fp32 operation (round-to-nearest-even, no
+ * fused multiply-add), and dequantizes as x = code * scale + bias.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  All memory is owned by
+ *     the caller; the library allocates no device memory and keeps no pointer
+ *     after a call returns.
+ *   - Calls are asynchronous and ordered on `stream`.
+ *   - Every argument that the host can see is validated before anything is
+ *     launched; on a non-OK status nothing was launched and no output is
+ *     touched.  kvq_last_error() then returns a message (thread-local).
+ *   - Faults inside kernels surface at the next synchronisation of `stream`.
+ *   - Sequence lengths live on the device and are read by the kernels; the
+ *     host-side max_len only sizes the launch.  Every len[b] must be in
+ *     [1, max_len] (prefill: [chunk, max_len]); otherwise results are
+ *     unspecified, though every memory access stays inside the cache.
+ *   - Calls that share one cache, workspace or output on one device must be
+ *     ordered (same stream or events); concurrent calls on such buffers race.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad count, Hq % Hkv != 0, ...      */
+    KVQ_ERR_UNSUPPORTED = 2,      /* bits not 4/8, group != 64, head_dim not 128/256/512 */
+    KVQ_ERR_CAPACITY = 3,         /* window > capacity, cache cannot hold the visible keys */
+    KVQ_ERR_WORKSPACE = 4,        /* workspace smaller than the *_workspace_bytes query  */
+    KVQ_ERR_HIP = 5               /* a HIP launch error                                   */
+} kvq_status;
+
+#define KVQ_GROUP_SIZE 64          /* values per quantization group along head_dim      */
+#define KVQ_V_BLOCK 8              /* cache slots per V code block                      */
+#define KVQ_MAX_SHARED_LAYERS 16   /* layers per kvq_shared_group                       */
+#define KVQ_MAX_SHARED_GROUPS 4    /* groups per kvq_attn_decode_shared call             */
+
+/*
+ * (host) Descriptor of one layer's cache.  R = capacity slots; a token at
+ * absolute position p lives in slot p mod R (a ring for sliding layers, a plain
+ * array for full layers, which need R >= every length).  Layouts, with
+ * B = batch, H = n_kv_heads, D = head_dim, G = D/64:
+ *
+ *   k_codes  uint32 [B][H][R][D*k_bits/32]   token-major: word w of a slot holds
+ *            elements [w*k, (w+1)*k) of head_dim, k = 32/k_bits, element e at bits
+ *            [k_bits*(e mod k), k_bits*(e mod k + 1))  (little-endian nibbles/bytes)
+ *   v_codes  uint32 [B][H][R/8][D][v_bits/4]  blocked: block n holds slots 8n..8n+7;
+ *            for each d its 8 codes are packed in v_bits/4 words, slot 8n+t at bits
+ *            [v_bits*t, v_bits*(t+1)) of the block's v_bits bytes (little-endian)
+ *   k_sb, v_sb  uint32 [B][H][R][G]  per slot and group: bf16 scale in bits 0..15,
+ *            bf16 bias in bits 16..31
+ *
+ * The blocked V layout puts the 8 codes of one head_dim element for 8
+ * consecutive slots in one place, which is what the value contraction over
+ * keys reads; keys are read along head_dim, so K stays token-major.
+ * Requirements: group_size == 64; head_dim in {128, 256, 512}; k_bits, v_bits in
+ * {4, 8}; capacity a positive multiple of 8; 0 <= window <= capacity (0: full).
+ */
+typedef struct {
+    uint32_t *k_codes;
+    uint32_t *v_codes;
+    uint32_t *k_sb;
+    uint32_t *v_sb;
+    int32_t batch;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t group_size;
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t capacity;
+    int32_t window;
+} kvq_cache;
+
+/*
+ * Quantize T new tokens per sequence and write them into the cache
+ * (page 80, model.ts attentionTraining: cache.appendWindow(keys, values) before
+ * the read; page 78, gemma4-e4b.ts Gemma4Layer.kv: affine width and group 64).
+ *   k, v   fp32 [B][H][T][D], keys after norm and RoPE, values after norm
+ *   T      (host) tokens per sequence, T >= 0 (0 is a no-op)
+ *   pos0   int32 [B], absolute position of each sequence's first new token (>= 0)
+ * Token t of sequence b goes to slot (pos0[b] + t) mod R.  With T > R only the
+ * last R tokens are written.  Slots that this call does not write keep their
+ * contents (a V block shared with untouched slots is read, merged and written).
+ * Inputs must be finite with |x| <= 1e38; outside that the written codes are
+ * unspecified.
+ */
+kvq_status kvq_append_quantize(const kvq_cache *cache,
+                               const float *k, const float *v,
+                               int32_t T, const int32_t *pos0,
+                               hipStream_t stream);
+
+/*
+ * One decode read: one query per sequence attends the cache
+ * (page 80, model.ts decode declaration and attentionTraining read.attend(q, scale)).
+ *   q      bf16 [B][Hq][D]; query head hq reads KV head hq / (Hq/Hkv)
+ *   len    int32 [B], tokens in the cache including this step's; the query sits at
+ *          p = len[b]-1 and sees positions max(0, p-W+1) .. p (W = window, 0: 0 .. p)
+ *   max_len (host) upper bound of len[b]; sizes the launch
+ *   scale  SDPA scale (1.0 for Gemma 4)
+ *   out    bf16 [B][Hq][D] = softmax(scale * q.K^T) V, rounded to nearest even
+ *   workspace  at least kvq_decode_workspace_bytes() bytes for the same arguments
+ *          (may be NULL when that is 0); holds split partials, needs no clearing
+ */
+kvq_status kvq_attn_decode(const kvq_cache *cache,
+                           const uint16_t *q, int32_t n_q_heads,
+                           const int32_t *len, int32_t max_len, float scale,
+                           uint16_t *out,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * One chunked-prefill read (page 80, model.ts prompt / promptChunk: a whole chunk
+ * of a prompt per sequence): the chunk's C tokens were appended first; query i of
+ * sequence b sits at p = len[b] - C + i and sees max(0, p-W+1) .. p -- causal
+ * inside the chunk, windowed across it.
+ *   q    bf16 [B][Hq][C][D];  out bf16 [B][Hq][C][D]
+ * Window layers need capacity >= window + C - 1 (the chunk must not overwrite a
+ * key its first query still sees); full layers need capacity >= max_len.
+ */
+kvq_status kvq_attn_prefill_chunk(const kvq_cache *cache,
+                                  const uint16_t *q, int32_t n_q_heads, int32_t chunk,
+                                  const int32_t *len, int32_t max_len, float scale,
+                                  uint16_t *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
+ * (host) One cache read by the queries of n_layers KV-sharing layers
+ * (page 80, model.ts header: KV-shared layers; page 78, gemma4-e4b.ts LAYERS:
+ * sharers attend the last donor of their type, whose read is made once).
+ *   q[l], out[l]  (host arrays of device pointers) bf16 [B][Hq][D] per layer
+ *   len, max_len, scale  as for kvq_attn_decode, shared by the group's layers
+ */
+typedef struct {
+    const kvq_cache *cache;
+    int32_t n_layers;
+    const uint16_t *const *q;
+    uint16_t *const *out;
+    int32_t n_q_heads;
+    float scale;
+    const int32_t *len;
+    int32_t max_len;
+} kvq_shared_group;
+
+/*
+ * Several shared groups, e.g. the sliding donor's sharers and the full donor's
+ * sharers of one decode step, in one attention launch (plus one combine
+ * launch).  Each layer's output equals a kvq_attn_decode of that layer alone.
+ * 1 <= n_groups <= KVQ_MAX_SHARED_GROUPS.
+ */
+kvq_status kvq_attn_decode_shared(const kvq_shared_group *groups, int32_t n_groups,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* (host) Workspace bytes for kvq_attn_decode_shared with these groups; for a
+ * kvq_attn_decode call pass one group with n_layers = 1.  Returns 0 when the
+ * call needs none, and SIZE_MAX when the arguments are invalid. */
+size_t kvq_decode_workspace_bytes(const kvq_shared_group *groups, int32_t n_groups);
+
+/* (host) Workspace bytes for kvq_attn_prefill_chunk with these arguments. */
+size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads,
+                                   int32_t chunk, int32_t max_len);
+
+/* (host) Message for the last non-OK status on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

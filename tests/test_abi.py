@@ -1,0 +1,126 @@
+"""The C ABI library: it loads, exports every entry point include/kvq.h declares, and
+its host-side validation returns the documented statuses.  No GPU is needed: every
+call here fails validation before anything reaches the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_group_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+FAKE = 0x100000  # a non-null address; validation fails before it is used
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return kvq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char \*)\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def cache(**kw):
+    c = dict(k_codes=FAKE, v_codes=FAKE, k_sb=FAKE, v_sb=FAKE, batch=2, n_kv_heads=2, head_dim=256,
+             group_size=64, k_bits=4, v_bits=8, capacity=512, window=512)
+    c.update(kw)
+    return kvq.CacheStruct(**c)
+
+
+def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAKE):
+    return lib.kvq_attn_decode(ctypes.byref(c), q, Hq, ln, max_len, scale, out, None, ws, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=100), 2), (dict(head_dim=64), 2), (dict(group_size=32), 2), (dict(k_bits=5), 2),
+    (dict(v_bits=2), 2), (dict(capacity=12), 1), (dict(capacity=0), 1), (dict(window=1024), 3),
+    (dict(window=-1), 1), (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(k_codes=0), 1),
+    (dict(v_sb=0), 1),
+])
+def test_decode_cache_validation(lib, kw, status):
+    assert decode(lib, cache(**kw)) == status
+    assert lib.kvq_last_error().decode()
+
+
+def test_decode_argument_validation(lib):
+    assert decode(lib, cache(), Hq=7) == 1            # Hq % Hkv
+    assert decode(lib, cache(), q=0) == 1
+    assert decode(lib, cache(), out=0) == 1
+    assert decode(lib, cache(), ln=0) == 1
+    assert decode(lib, cache(), max_len=0) == 1
+    assert decode(lib, cache(), scale=float("inf")) == 1
+    full = cache(window=0, capacity=1024)
+    assert decode(lib, full, max_len=2048) == 3       # full cache cannot hold max_len
+    big = cache(window=0, capacity=32768, head_dim=512, n_kv_heads=1, k_bits=8, v_bits=8, batch=4)
+    assert decode(lib, big, max_len=32768, ws=0) == 4  # split partials need a workspace
+    assert "workspace" in lib.kvq_last_error().decode()
+
+
+def test_prefill_validation(lib):
+    c = cache(window=512, capacity=1024)
+    f = lib.kvq_attn_prefill_chunk
+    assert f(ctypes.byref(c), FAKE, 8, 600, FAKE, 9000, 1.0, FAKE, None, 0, None) == 3   # W + C - 1 > R
+    assert f(ctypes.byref(c), FAKE, 8, 0, FAKE, 9000, 1.0, FAKE, None, 0, None) == 1     # chunk 0
+    assert f(ctypes.byref(c), FAKE, 8, 512, FAKE, 100, 1.0, FAKE, None, 0, None) == 1    # max_len < chunk
+
+
+def test_append_validation(lib):
+    c = cache()
+    f = lib.kvq_append_quantize
+    assert f(ctypes.byref(c), FAKE, FAKE, -1, FAKE, None) == 1
+    assert f(ctypes.byref(c), FAKE, FAKE, 0, FAKE, None) == 0        # T == 0 is a no-op
+    assert f(ctypes.byref(c), 0, FAKE, 4, FAKE, None) == 1
+    assert f(ctypes.byref(c), FAKE + 4, FAKE, 4, FAKE, None) == 1    # k not 16-byte aligned
+    assert f(ctypes.byref(cache(head_dim=96)), FAKE, FAKE, 4, FAKE, None) == 2
+
+
+def _group(c, n_layers=1, Hq=8, max_len=4096):
+    qa = (ctypes.c_void_p * max(n_layers, 1))(*([FAKE] * max(n_layers, 1)))
+    oa = (ctypes.c_void_p * max(n_layers, 1))(*([FAKE] * max(n_layers, 1)))
+    return kvq.SharedGroupStruct(ctypes.pointer(c), n_layers, qa, oa, Hq, 1.0, FAKE, max_len), (qa, oa)
+
+
+def test_shared_validation_and_workspace_query(lib):
+    c = cache()
+    g, keep = _group(c, 3)
+    arr = (kvq.SharedGroupStruct * 1)(g)
+    assert lib.kvq_attn_decode_shared(arr, 0, None, 0, None) == 1
+    assert lib.kvq_attn_decode_shared(arr, 5, None, 0, None) == 1
+    bad, keep2 = _group(c, 17)
+    assert lib.kvq_attn_decode_shared((kvq.SharedGroupStruct * 1)(bad), 1, None, 0, None) == 1
+    assert lib.kvq_decode_workspace_bytes((kvq.SharedGroupStruct * 1)(bad), 1) == kvq.SIZE_MAX
+    n = lib.kvq_decode_workspace_bytes(arr, 1)
+    assert n != kvq.SIZE_MAX
+    big = cache(window=0, capacity=32768, head_dim=512, n_kv_heads=1, k_bits=8, v_bits=8, batch=4)
+    gb, keep3 = _group(big, 1, 8, 32768)
+    need = lib.kvq_decode_workspace_bytes((kvq.SharedGroupStruct * 1)(gb), 1)
+    assert 0 < need < (1 << 30)
+    # a workspace one byte short is refused
+    assert lib.kvq_attn_decode_shared((kvq.SharedGroupStruct * 1)(gb), 1, FAKE, need - 1, None) == 4
+
+
+def test_prefill_workspace_query(lib):
+    c = cache(window=512, capacity=1024)
+    assert lib.kvq_prefill_workspace_bytes(ctypes.byref(c), 8, 512, 8704) != kvq.SIZE_MAX
+    assert lib.kvq_prefill_workspace_bytes(ctypes.byref(c), 7, 512, 8704) == kvq.SIZE_MAX
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    c = kvq.KVCache.__new__(kvq.KVCache)
+    with pytest.raises(kvq.KvqUnavailable):
+        kvq.kvq_append_quantize(c, torch.zeros(1, 1, 1, 128), torch.zeros(1, 1, 1, 128), torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,194 @@
+"""GPU attention (decode, KV-shared decode, chunked prefill) against the fp64 oracle.
+
+Tolerance: bf16 outputs within max-abs 1e-2 and mean-abs 1e-3 of the oracle.
+The GPU appends its own cache (bit-exact with the oracle's, see test_gpu_append)
+and the oracle attends its own cache; the two share only the seeded draws."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_group_amd as kvq
+import oracle
+from kvq_testutil import assert_close, build_workload, torch_bf16_to_f64
+from synth import WORKLOADS, small_q_bits, small_randn
+
+pytestmark = pytest.mark.gpu
+
+
+def q_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def make_pair(B, H, D, kb, vb, R, W, L, seed, zero=True):
+    g = kvq.KVCache(B, H, D, kb, vb, R, window=W, zero=zero)
+    o = oracle.Cache(B, H, D, R, kb, vb, window=W)
+    k = small_randn(seed, (B, H, L, D), D ** -0.25)
+    v = small_randn(seed + 1, (B, H, L, D), D ** -0.25)
+    for t0 in range(0, L, 300):
+        t1 = min(L, t0 + 300)
+        pos0 = np.full(B, t0, np.int32)
+        kvq.kvq_append_quantize(g, torch.from_numpy(k[:, :, t0:t1].copy()).cuda(),
+                                torch.from_numpy(v[:, :, t0:t1].copy()).cuda(), torch.from_numpy(pos0).cuda())
+        o.append(k[:, :, t0:t1], v[:, :, t0:t1], pos0)
+    return g, o
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, D, kb, vb, R, W, L
+    (1, 8, 2, 256, 4, 4, 128, 0, 128),
+    (2, 8, 2, 256, 4, 8, 512, 512, 1500),     # ring wrap
+    (2, 8, 1, 512, 8, 8, 2048, 0, 2000),      # full, cache not full (garbage-free zeros)
+    (3, 4, 4, 128, 8, 4, 256, 100, 700),      # MHA, window < R
+    (1, 16, 1, 512, 4, 8, 64, 0, 1),          # a single key
+    (2, 24, 2, 128, 4, 4, 96, 40, 333),       # 12 rows per KV head
+    (1, 40, 2, 256, 8, 8, 160, 0, 150),       # 20 rows: two row tiles
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_small(case):
+    B, Hq, Hkv, D, kb, vb, R, W, L = case
+    print(f"decode {case}", flush=True)
+    g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case))
+    q = small_q_bits(sum(case) + 7, (B, Hq, 1, D), D ** -0.25)
+    lens = np.array([L - (b % 2) * min(3, L - 1) for b in range(B)], np.int32)
+    out = kvq.kvq_attn_decode(g, q_dev(q[:, :, 0].copy()), torch.from_numpy(lens).cuda(), int(lens.max()))
+    torch.cuda.synchronize()
+    ref = o.attend(q, lens)[:, :, 0]
+    assert_close(torch_bf16_to_f64(out), ref, f"decode {case}")
+
+
+def test_decode_garbage_slots():
+    """Slots beyond len hold arbitrary bits (torch.empty); they must not leak into the output."""
+    B, Hq, Hkv, D, R, L = 2, 8, 1, 512, 256, 77
+    g = kvq.KVCache(B, Hkv, D, 8, 8, R, window=0, zero=False)
+    for t in (g.k_codes, g.v_codes, g.k_sb, g.v_sb):
+        t.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, t.shape, dtype=torch.int32, device="cuda"))
+    o = oracle.Cache(B, Hkv, D, R, 8, 8)
+    k = small_randn(1, (B, Hkv, L, D), 0.21)
+    v = small_randn(2, (B, Hkv, L, D), 0.21)
+    kvq.kvq_append_quantize(g, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                            torch.zeros(B, dtype=torch.int32, device="cuda"))
+    o.append(k, v, np.zeros(B, np.int32))
+    q = small_q_bits(3, (B, Hq, 1, D), 0.21)
+    lens = np.array([L, 40], np.int32)
+    out = kvq.kvq_attn_decode(g, q_dev(q[:, :, 0].copy()), torch.from_numpy(lens).cuda(), 256)
+    torch.cuda.synchronize()
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens)[:, :, 0], "garbage slots")
+
+
+def test_decode_split_invariance_and_determinism():
+    B, Hq, Hkv, D, R, L = 2, 8, 1, 512, 4096, 4000
+    g, o = make_pair(B, Hkv, D, 8, 8, R, 0, L, seed=5)
+    q = q_dev(small_q_bits(6, (B, Hq, D), 0.21))
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    outs = []
+    try:
+        for s in ("1", "3", "16", "64"):
+            os.environ["KVQ_SPLITS"] = s
+            outs.append(kvq.kvq_attn_decode(g, q, lens, L).clone())
+        again = kvq.kvq_attn_decode(g, q, lens, L)
+    finally:
+        os.environ.pop("KVQ_SPLITS", None)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[-1], again)                      # same plan: bitwise
+    ref = o.attend(small_q_bits(6, (B, Hq, D), 0.21)[:, :, None], np.full(B, L, np.int32))[:, :, 0]
+    for x in outs:
+        assert_close(torch_bf16_to_f64(x), ref, "split")
+
+
+@pytest.mark.parametrize("name", ["decode_b1_l128", "sliding_decode_b8_w512", "full_decode_b4_l32768"])
+def test_decode_workload(name):
+    wl = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    gpu, orc, qd, _ = build_workload(wl)
+    spec = wl.caches[0]
+    q = qd[0][0]                                             # [B][Hq][1][D]
+    lens = np.full(spec.B, spec.length, np.int32)
+    out = kvq.kvq_attn_decode(gpu["kv"], q_dev(q[:, :, 0].copy()), torch.from_numpy(lens).cuda(), spec.length)
+    torch.cuda.synchronize()
+    o, _ = orc["kv"]
+    ref = o.attend(q, lens)[:, :, 0]
+    mx, mean = assert_close(torch_bf16_to_f64(out), ref, name)
+    print(f"{name}: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
+def test_shared_equals_separate_small():
+    B, Hkv, D, R, W, L = 2, 2, 256, 512, 512, 1000
+    g, o = make_pair(B, Hkv, D, 4, 4, R, W, L, seed=40)
+    g2, o2 = make_pair(B, 1, 512, 8, 8, 1024, 0, L, seed=41)
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    qa = [q_dev(small_q_bits(50 + i, (B, 8, D), 0.25)) for i in range(3)]
+    qb = [q_dev(small_q_bits(60, (B, 8, 512), 0.21))]
+    try:
+        os.environ["KVQ_SPLITS"] = "2"
+        outs = kvq.kvq_attn_decode_shared([kvq.SharedGroup(g, qa, lens, L), kvq.SharedGroup(g2, qb, lens, L)])
+        sep_a = [kvq.kvq_attn_decode(g, q, lens, L) for q in qa]
+        sep_b = [kvq.kvq_attn_decode(g2, q, lens, L) for q in qb]
+    finally:
+        os.environ.pop("KVQ_SPLITS", None)
+    torch.cuda.synchronize()
+    for x, y in zip(outs[0] + outs[1], sep_a + sep_b):
+        assert torch.equal(x, y)
+    lens_np = np.full(B, L, np.int32)
+    for i in range(3):
+        ref = o.attend(small_q_bits(50 + i, (B, 8, D), 0.25)[:, :, None], lens_np)[:, :, 0]
+        assert_close(torch_bf16_to_f64(outs[0][i]), ref, f"shared layer {i}")
+
+
+def test_shared_workload():
+    wl = WORKLOADS["shared_decode_b32"]
+    sample = [0, 13, 31]
+    print("workload shared_decode_b32", flush=True)
+    gpu, orc, qd, _ = build_workload(wl, oracle_batches={"full": sample})
+    donor, full = wl.cache("donor"), wl.cache("full")
+    lens = torch.full((donor.B,), donor.length, dtype=torch.int32, device="cuda")
+    qa = [q_dev(x[:, :, 0].copy()) for x in qd[0]]
+    qb = [q_dev(x[:, :, 0].copy()) for x in qd[1]]
+    outs = kvq.kvq_attn_decode_shared([kvq.SharedGroup(gpu["donor"], qa, lens, donor.length),
+                                       kvq.SharedGroup(gpu["full"], qb, lens, full.length)])
+    torch.cuda.synchronize()
+    od, _ = orc["donor"]
+    lens_np = np.full(donor.B, donor.length, np.int32)
+    for i, x in enumerate(qd[0]):
+        assert_close(torch_bf16_to_f64(outs[0][i]), od.attend(x, lens_np)[:, :, 0], f"donor layer {i}")
+    of, sel = orc["full"]
+    ref = of.attend(qd[1][0][sel], lens_np[sel])[:, :, 0]
+    assert_close(torch_bf16_to_f64(outs[1][0])[sel], ref, "full layer")
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, D, kb, vb, R, W, L, C
+    (1, 8, 2, 256, 4, 4, 128, 100, 300, 29),
+    (2, 4, 1, 128, 8, 8, 256, 0, 200, 64),
+    (1, 8, 2, 256, 4, 8, 1024, 512, 2000, 512),
+    (2, 2, 2, 512, 8, 4, 96, 48, 150, 17),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_small(case):
+    B, Hq, Hkv, D, kb, vb, R, W, L, C = case
+    print(f"prefill {case}", flush=True)
+    g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case))
+    q = small_q_bits(sum(case) + 1, (B, Hq, C, D), D ** -0.25)
+    lens = np.full(B, L, np.int32)
+    out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+    torch.cuda.synchronize()
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill {case}")
+
+
+def test_prefill_workload():
+    wl = WORKLOADS["prefill_b2_c512_w512"]
+    print("workload prefill_b2_c512_w512", flush=True)
+    gpu, orc, qd, _ = build_workload(wl)
+    spec = wl.caches[0]
+    q = qd[0][0]
+    lens = np.full(spec.B, spec.length, np.int32)
+    out = kvq.kvq_attn_prefill_chunk(gpu["kv"], q_dev(q), torch.from_numpy(lens).cuda(), spec.length)
+    torch.cuda.synchronize()
+    o, _ = orc["kv"]
+    mx, mean = assert_close(torch_bf16_to_f64(out), o.attend(q, lens), "prefill workload")
+    print(f"prefill: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
