@@ -23,27 +23,32 @@
 // Each workgroup has 4 waves that take alternate steps of its key range and
 // merge (max, sum, output) through LDS at the end; a split with S > 1 leaves
 // fp32 partials that the combine kernel reduces.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 
-constexpr int kWaves = 4;
-
-constexpr int kMergeChunk = 256;   // head_dim columns merged per LDS round
+// Waves of a workgroup split head_dim: wave w owns the quantization groups
+// [w*GPW, (w+1)*GPW).  All waves walk the same 32-key steps; each computes a
+// partial S^T over its groups, the partials meet in LDS (one barrier per step,
+// double-buffered by step parity), every wave then holds the full scores and
+// the same softmax state, and accumulates O^T for its own head_dim columns.
+template <int D>
+struct Shape {
+    static constexpr int G = D / 64;
+    static constexpr int NW = G >= 4 ? 4 : G;      // waves per workgroup
+    static constexpr int GPW = G / NW;              // groups per wave
+    static constexpr int DTW = 4 * GPW;             // 16-column tiles of O^T per wave
+};
 
 template <int D>
 struct AttnSmem {
-    static constexpr int G = D / 64;
-    union {
-        struct {
-            uint32_t k_kg[kWaves][kStep][G];   // K scale|bias, key-major
-            uint32_t k_gk[kWaves][G][kStep];   // K scale|bias, group-major
-            uint32_t v_gk[kWaves][G][kStep];   // V scale|bias, group-major
-        } sb;
-        float mrg[kWaves - 1][kRowTile][kMergeChunk + 4];
-    } u;
-    float ml[kWaves][kRowTile][2];
+    static constexpr int NW = Shape<D>::NW, GPW = Shape<D>::GPW;
+    f32x4 spart[2][NW][2][kWave];          // partial S^T tiles, [step parity][wave][tile][lane]
+    uint32_t ksb[NW][GPW][kStep];          // this step's K scale|bias words, per wave, group-major
+    uint32_t vsb[NW][GPW][kStep];          // V scale|bias words
 };
 
 struct RowMap {
@@ -62,18 +67,27 @@ __device__ __forceinline__ RowMap map_row(const AttnDesc& P, int hkv, int grow)
 
 __device__ __forceinline__ int wrap(int slot, int R) { return slot >= R ? slot - R : slot; }
 
+// Registers holding one step's codes and scale|bias words (the prefetch unit).
+template <int D, int KB, int VB>
+struct StepRegs {
+    static constexpr int GPW = Shape<D>::GPW, DTW = Shape<D>::DTW;
+    typename std::conditional<KB == 8, u32x4, u32x2>::type kc[2][GPW];
+    typename std::conditional<VB == 8, u32x2, uint32_t>::type vc[DTW];
+    uint32_t ksb, vsb;
+};
+
 template <int D, int KB, int VB>
 __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D>& sm)
 {
-    constexpr int G = D / 64;
-    constexpr int DT = D / 16;
+    using Sh = Shape<D>;
+    constexpr int G = Sh::G, NW = Sh::NW, GPW = Sh::GPW, DTW = Sh::DTW;
     constexpr int KW = D * KB / 32;      // K words per slot
     constexpr int VW = VB / 4;           // V words per (block, d)
-    constexpr int NL = G / 2;            // scale|bias words each lane stages per step
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, lg = lane >> 4;
+    const int g0 = wave * GPW;           // first group of this wave
 
     const int S = P.S;
     const int s = idx % S;
@@ -104,18 +118,20 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     int khi = min(j1 - 1, p_row);
     if (!row_ok) { klo = 1; khi = 0; }
 
-    // ---- q as MFMA B operand (fp16, element order matching the K code order),
-    //      and the per-group sums Q_g for the bias term
-    f16x8 qf[G][2];
-    float qsum[G];
+    // ---- q of this wave's groups as MFMA B operand (fp16, element order matching
+    //      the K code order), and the group sums Q_g for the bias term
+    f16x8 qf[GPW][2];
+    bf16x8 qb;
     {
         const uint16_t* qrow = P.q[rm.layer] + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
+        float qsum[GPW];
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
+        for (int gi = 0; gi < GPW; ++gi) {
+            const int gg = g0 + gi;
             u32x4 u0 = 0, u1 = 0;
             if (row_ok) {
-                u0 = *reinterpret_cast<const u32x4*>(qrow + gi * 64 + lg * 16);
-                u1 = *reinterpret_cast<const u32x4*>(qrow + gi * 64 + lg * 16 + 8);
+                u0 = *reinterpret_cast<const u32x4*>(qrow + gg * 64 + lg * 16);
+                u1 = *reinterpret_cast<const u32x4*>(qrow + gg * 64 + lg * 16 + 8);
             }
             float f[16];
 #pragma unroll
@@ -136,14 +152,12 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
                 qf[gi][1][e] = (_Float16)f[8 + e0];
             }
         }
-    }
-    bf16x8 qb;
-    {
+        // k-slots 8*lg + e: Q_g split in three bf16 parts (lg = 0, 1, 2) for group g0+e
         u32x4 w = 0;
         if (lg < 3) {
             uint16_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
+            for (int gi = 0; gi < GPW; ++gi) {
                 const float q1 = __uint_as_float((uint32_t)f32_to_bf16_rne(qsum[gi]) << 16);
                 const float r1 = qsum[gi] - q1;
                 const float q2 = __uint_as_float((uint32_t)f32_to_bf16_rne(r1) << 16);
@@ -159,55 +173,71 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     }
 
     const float sl2e = P.scale_log2e;
-    f32x4 O[DT];
+    f32x4 O[DTW];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DTW; ++dt) O[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     f32x4 corr = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
     const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
     const int st0 = j0 & ~(kStep - 1);
     const int64_t kslot0 = (int64_t)bh * R;
-    const uint32_t* kcodes = P.k_codes;
-    const uint32_t* vcodes = P.v_codes;
+    const uint32_t* __restrict__ kcodes = P.k_codes;
+    const uint32_t* __restrict__ vcodes = P.v_codes;
+    // lane -> (key, group) of the scale|bias word it stages each step
+    const int sb_key = GPW == 2 ? lane >> 1 : lane & 31;
+    const int sb_g = GPW == 2 ? lane & 1 : 0;
+    const bool sb_on = GPW == 2 || lane < 32;
 
-    for (int si = wave; si < nsteps; si += kWaves) {
-        const int st = st0 + si * kStep;
+    auto load_step = [&](StepRegs<D, KB, VB>& r, int st) {
         const int st_mod = st % R;
-
-        // ---- stage this step's scale|bias words in LDS
-        {
-            const int kk = lane >> 1, g0 = (lane & 1) * NL;
-            const int slot = wrap(st_mod + kk, R);
-            const uint32_t* ks = P.k_sb + (kslot0 + slot) * G + g0;
-            const uint32_t* vs = P.v_sb + (kslot0 + slot) * G + g0;
+        // scale|bias words first: they are the first thing a step consumes
+        const int64_t sbi = (kslot0 + wrap(st_mod + sb_key, R)) * G + g0 + sb_g;
+        r.ksb = P.k_sb[sb_on ? sbi : kslot0 * G];
+        r.vsb = P.v_sb[sb_on ? sbi : kslot0 * G];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const uint32_t kw = ks[i], vw = vs[i];
-                sm.u.sb.k_kg[wave][kk][g0 + i] = kw;
-                sm.u.sb.k_gk[wave][g0 + i][kk] = kw;
-                sm.u.sb.v_gk[wave][g0 + i][kk] = vw;
+        for (int t = 0; t < 2; ++t) {
+            const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
+            const uint32_t* krow = kcodes + (kslot0 + wrap(st_mod + kk, R)) * KW;
+#pragma unroll
+            for (int gi = 0; gi < GPW; ++gi) {
+                if constexpr (KB == 8) r.kc[t][gi] = *reinterpret_cast<const u32x4*>(krow + (g0 + gi) * 16 + lg * 4);
+                else r.kc[t][gi] = *reinterpret_cast<const u32x2*>(krow + (g0 + gi) * 8 + lg * 2);
             }
+        }
+        const int vslot = wrap(st_mod + 8 * lg, R);
+        const uint32_t* vrow = vcodes + (((int64_t)bh * (R / 8) + (vslot >> 3)) * D + 64 * g0 + m) * VW;
+#pragma unroll
+        for (int dd = 0; dd < DTW; ++dd) {
+            if constexpr (VB == 8) r.vc[dd] = *reinterpret_cast<const u32x2*>(vrow + 16 * dd * VW);
+            else r.vc[dd] = vrow[16 * dd * VW];
+        }
+    };
+
+    // One step: stage scale|bias, partial scores, exchange, softmax, PV.
+    // `par` alternates the LDS score buffer between consecutive steps.
+    auto compute_step = [&](const StepRegs<D, KB, VB>& cr, int st, int par) {
+        // ---- stage the step's scale|bias words in this wave's LDS region
+        if (sb_on) {
+            sm.ksb[wave][sb_g][sb_key] = cr.ksb;
+            sm.vsb[wave][sb_g][sb_key] = cr.vsb;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // ---- S^T = K Q^T for the step's two 16-key tiles.  Tile t row r holds
-        //      key 8*(r/4) + 4*t + r%4, so lane group lg ends with keys 8*lg .. 8*lg+7.
-        float z[8];
+        // ---- partial S^T over this wave's groups.  Tile t row r holds key
+        //      8*(r/4) + 4*t + r%4, so lane group lg ends with keys 8*lg .. 8*lg+7.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
-            const int slot = wrap(st_mod + kk, R);
-            const uint32_t* krow = kcodes + (kslot0 + slot) * KW;
             bf16x8 ab;
             {
                 u32x4 w = 0;
                 if (lg < 3) {
-                    uint32_t bw[8];
+                    uint32_t bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bw[e] = e < G ? sm.u.sb.k_kg[wave][kk][e < G ? e : 0] >> 16 : 0u;
+                    for (int e = 0; e < GPW; ++e) bw[e] = sm.ksb[wave][e][kk] >> 16;
                     w = (u32x4){bw[0] | (bw[1] << 16), bw[2] | (bw[3] << 16),
                                 bw[4] | (bw[5] << 16), bw[6] | (bw[7] << 16)};
                 }
@@ -215,30 +245,33 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             }
             f32x4 sacc = mfma_bf16(ab, qb, (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) {
+            for (int gi = 0; gi < GPW; ++gi) {
                 f16x8 a0, a1;
-                if constexpr (KB == 8) {
-                    const u32x4 w = *reinterpret_cast<const u32x4*>(krow + gi * 16 + lg * 4);
-                    codes8x16_to_f16(w, a0, a1);
-                } else {
-                    const u32x2 w = *reinterpret_cast<const u32x2*>(krow + gi * 8 + lg * 2);
-                    a0 = codes4x8_to_f16(w.x);
-                    a1 = codes4x8_to_f16(w.y);
-                }
+                if constexpr (KB == 8) codes8x16_to_f16(cr.kc[t][gi], a0, a1);
+                else { a0 = codes4x8_to_f16(cr.kc[t][gi].x); a1 = codes4x8_to_f16(cr.kc[t][gi].y); }
                 f32x4 x = mfma_f16(a0, qf[gi][0], (f32x4){0.f, 0.f, 0.f, 0.f});
                 x = mfma_f16(a1, qf[gi][1], x);
-                const u32x4 sw = *reinterpret_cast<const u32x4*>(&sm.u.sb.k_gk[wave][gi][8 * lg + 4 * t]);
+                const u32x4 sw = *reinterpret_cast<const u32x4*>(&sm.ksb[wave][gi][8 * lg + 4 * t]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sacc[i] += bf16_lo_to_f32(sw[i]) * x[i];
             }
+            sm.spart[par][wave][t][lane] = sacc;
+        }
+        __syncthreads();
+
+        // ---- full scores (same in every wave) and the online softmax, base 2
+        float z[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 sacc = sm.spart[par][0][t][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sacc += sm.spart[par][w][t][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = st + 8 * lg + 4 * t + i;
                 z[4 * t + i] = (key >= klo && key <= khi) ? sacc[i] * sl2e : -INFINITY;
             }
         }
-
-        // ---- online softmax (base 2); one query row per lane, max over the 4 lane groups
         float mloc = z[0];
 #pragma unroll
         for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, z[k]);
@@ -253,14 +286,14 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         m_run = m_new;
         if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+            for (int dt = 0; dt < DTW; ++dt) O[dt] *= alpha;
             corr *= alpha;
         }
 
-        // ---- O^T += V^T (P * s_v)^T per group, and the bias term for all groups
-        // vk: key visible to this lane's query row (B side, per row);
-        // kin: key inside the item's range, i.e. its slot holds real data (A side,
-        // shared by all rows -- an A row here is a quantization group, not a query row).
+        // ---- O^T += V^T (P * s_v)^T per group; the bias term of all groups in one MFMA.
+        //      vk: key visible to this lane's query row (B side, per row).  kin: key
+        //      inside the item's range, so its slot holds data (A side, where a row
+        //      is a quantization group and not a query row).
         bool vk[8], kin[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -271,9 +304,9 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         {
             f16x8 pb, ac;
             u32x4 w0 = 0, w1 = 0;
-            if (m < G) {
-                w0 = *reinterpret_cast<const u32x4*>(&sm.u.sb.v_gk[wave][m < G ? m : 0][8 * lg]);
-                w1 = *reinterpret_cast<const u32x4*>(&sm.u.sb.v_gk[wave][m < G ? m : 0][8 * lg + 4]);
+            if (m < GPW) {
+                w0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg]);
+                w1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg + 4]);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -284,12 +317,10 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             }
             corr = mfma_f16(ac, pb, corr);
         }
-        const int vslot = wrap(st_mod + 8 * lg, R);
-        const uint32_t* vrow = vcodes + (((int64_t)bh * (R / 8) + (vslot >> 3)) * D + m) * VW;
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            const u32x4 s0 = *reinterpret_cast<const u32x4*>(&sm.u.sb.v_gk[wave][gi][8 * lg]);
-            const u32x4 s1 = *reinterpret_cast<const u32x4*>(&sm.u.sb.v_gk[wave][gi][8 * lg + 4]);
+        for (int gi = 0; gi < GPW; ++gi) {
+            const u32x4 s0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][gi][8 * lg]);
+            const u32x4 s1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][gi][8 * lg + 4]);
             f16x8 bs;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -301,82 +332,60 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             for (int dd = 0; dd < 4; ++dd) {
                 const int dt = 4 * gi + dd;
                 f16x8 a;
-                if constexpr (VB == 8) a = codes8x8_to_f16(*reinterpret_cast<const u32x2*>(vrow + 16 * dt * VW));
-                else a = codes4x8_to_f16(vrow[16 * dt * VW]);
+                if constexpr (VB == 8) a = codes8x8_to_f16(cr.vc[dt]);
+                else a = codes4x8_to_f16(cr.vc[dt]);
                 O[dt] = mfma_f16(a, bs, O[dt]);
             }
         }
+    };
+
+    // Ping-pong between two register sets so the next step's loads stay in
+    // flight while this step computes (a register copy would force a wait).
+    // The loads are issued unconditionally (the step index is clamped, so past
+    // the end the last step is read again and hits L2): a load under a branch
+    // would make the wait counters fall back to waiting for every load.
+    StepRegs<D, KB, VB> ra, rb;
+    const int last = max(nsteps - 1, 0);
+    if (nsteps > 0) load_step(ra, st0);
+    for (int si = 0; si < nsteps; si += 2) {
+        const int st = st0 + si * kStep;
+        load_step(rb, st0 + min(si + 1, last) * kStep);
+        compute_step(ra, st, 0);
+        if (si + 1 >= nsteps) break;
+        load_step(ra, st0 + min(si + 2, last) * kStep);
+        compute_step(rb, st + kStep, 1);
     }
 
-    // ---- fold the bias term into O: lane (m, lg) holds corr[group 4*lg+i][row m]
-    const float l_row = sum_across_groups(l_run);
+    // ---- fold the bias term into O: lane (m, lg) holds corr[group row 4*lg+i][query row m]
+    const float L = sum_across_groups(l_run);
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
+    for (int gi = 0; gi < GPW; ++gi) {
         const float c = __shfl(corr[gi & 3], m + 16 * (gi >> 2));
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) O[4 * gi + dd] += c;
     }
-
-    // ---- merge the 4 waves through LDS, kMergeChunk columns at a time
-    __syncthreads();                                   // all waves are done with the sb area
-    if (lg == 0) { sm.ml[wave][m][0] = m_run; sm.ml[wave][m][1] = l_row; }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.ml[w][m][0]);
-    float L = 0.0f, scl0 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.ml[w][m][0];
-        const float sw = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        L += sw * sm.ml[w][m][1];
-        if (w == 0) scl0 = sw;
-    }
-    const float scl_self = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-    constexpr int TPC = kMergeChunk / 16;              // d-tiles per merge chunk
-#pragma unroll
-    for (int c = 0; c < (DT + TPC - 1) / TPC; ++c) {
-        if (wave > 0) {
-            float* dst = &sm.u.mrg[wave - 1][m][4 * lg];
-#pragma unroll
-            for (int dt = c * TPC; dt < (c + 1) * TPC && dt < DT; ++dt)
-                *reinterpret_cast<f32x4*>(dst + 16 * (dt - c * TPC)) = O[dt] * scl_self;
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int dt = c * TPC; dt < (c + 1) * TPC && dt < DT; ++dt) {
-                f32x4 acc = O[dt] * scl0;
-#pragma unroll
-                for (int w = 1; w < kWaves; ++w)
-                    acc += *reinterpret_cast<const f32x4*>(&sm.u.mrg[w - 1][m][16 * (dt - c * TPC) + 4 * lg]);
-                O[dt] = acc;
-            }
-        }
-        __syncthreads();
-    }
-    if (wave != 0 || !row_ok) return;
-
+    if (!row_ok) return;
+    const int dcol = 64 * g0 + 4 * lg;   // + 16 * dt + i
     if (S == 1) {
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         uint16_t* orow = P.out[rm.layer] + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < DTW; ++dt) {
             const f32x4 o = O[dt] * inv;
             uint2 w;
             w.x = f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
             w.y = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-            *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * lg) = w;
+            *reinterpret_cast<uint2*>(orow + dcol + 16 * dt) = w;
         }
     } else {
         const int64_t ib = (int64_t)bh * P.n_rt + rt;
         const int64_t prow = (ib * S + s) * kRowTile + m;
         float* po = P.part + prow * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * lg) = O[dt];
-        if (lg == 0) {
+        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
+        if (wave == 0 && lg == 0) {
             float* pml = P.part + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
-            pml[0] = M;
+            pml[0] = m_run;
             pml[1] = L;
         }
     }
@@ -390,7 +399,7 @@ __device__ __forceinline__ int find_desc(const AttnParams& P, int bid)
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams P)
+__global__ __launch_bounds__(64 * Shape<D>::NW) void attn_kernel(AttnParams P)
 {
     __shared__ AttnSmem<D> sm;
     const int bid = blockIdx.x;
@@ -423,69 +432,87 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
     }
 }
 
+// One workgroup per (descriptor, row tile item, row, 64-column chunk):
+// out = sum_s w_s o_s / sum_s w_s l_s, w_s = 2^(m_s - max m).  The 256 threads
+// are 16 column quads x 16 split lanes; each split lane sums every 16th split
+// and the 16 sums meet in LDS.  Splits that saw no key (m_s = -inf) are skipped.
+constexpr int kCombCols = 64;
+
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
 {
-    __shared__ float wts[kRowTile][kMaxSplits];
+    __shared__ float wts[kMaxSplits];
+    __shared__ f32x4 red[16][16];
     const int bid = blockIdx.x;
     int di = -1;
     for (int i = 0; i < P.n_desc; ++i)
         if (P.d[i].S > 1 && bid >= P.d[i].comb_begin) di = i;
     if (di < 0) return;
     const AttnDesc& d = P.d[di];
-    const int ib = bid - d.comb_begin;
+    const int S = d.S, D = d.D;
+    const int nch = D / kCombCols;
+    int ir = bid - d.comb_begin;
+    const int ch = ir % nch;
+    ir /= nch;
+    const int r = ir % kRowTile;
+    const int ib = ir / kRowTile;
     const int rt = ib % d.n_rt;
     const int bh = ib / d.n_rt;
     const int b = bh / d.Hkv, hkv = bh - b * d.Hkv;
-    const int S = d.S, D = d.D;
+    const int grow = rt * kRowTile + r;
+    if (grow >= d.n_rows) return;
     const float* po = d.part;
     const float* pml = d.part + (size_t)d.B * d.Hkv * d.n_rt * S * kRowTile * D;
     const int tid = threadIdx.x;
-    if (tid < kRowTile) {
-        const int64_t r0 = ((int64_t)ib * S) * kRowTile + tid;
+    if (tid < 64) {
         float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, pml[(r0 + (int64_t)s * kRowTile) * 2]);
+        for (int s = tid; s < S; s += 64) M = fmaxf(M, pml[(((int64_t)ib * S + s) * kRowTile + r) * 2]);
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
         float L = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            const float ms = pml[(r0 + (int64_t)s * kRowTile) * 2];
-            const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-            wts[tid][s] = w;
-            L += w * pml[(r0 + (int64_t)s * kRowTile) * 2 + 1];
+        for (int s = tid; s < S; s += 64) {
+            const float* ml = pml + (((int64_t)ib * S + s) * kRowTile + r) * 2;
+            const float w = ml[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M);
+            wts[s] = w;
+            L += w * ml[1];
         }
+        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        for (int s = 0; s < S; ++s) wts[tid][s] *= inv;
+        for (int s = tid; s < S; s += 64) wts[s] *= inv;
     }
     __syncthreads();
-    const int D4 = D / 4;
-    for (int e = tid; e < kRowTile * D4; e += blockDim.x) {
-        const int r = e / D4, d4 = e - r * D4;
-        const int grow = rt * kRowTile + r;
-        if (grow >= d.n_rows) continue;
-        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const float w = wts[r][s];
-            if (w == 0.0f) continue;
-            acc += w * *reinterpret_cast<const f32x4*>(po + ((((int64_t)ib * S + s) * kRowTile + r) * D + 4 * d4));
-        }
-        const RowMap rm = map_row(d, hkv, grow);
-        uint16_t* orow = d.out[rm.layer] + ((((int64_t)b * d.Hq + rm.hq) * d.C + rm.qi) * D);
-        uint2 w;
-        w.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-        w.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-        *reinterpret_cast<uint2*>(orow + 4 * d4) = w;
+    const int q4 = tid & 15;           // column quad within the chunk
+    const int sl = tid >> 4;           // split lane
+    const int col = ch * kCombCols + 4 * q4;
+    const float* src = po + (((int64_t)ib * S) * kRowTile + r) * D + col;
+    const int64_t sstride = (int64_t)kRowTile * D;
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s = sl; s < S; s += 16) {
+        const float w = wts[s];
+        if (w != 0.0f) acc += w * *reinterpret_cast<const f32x4*>(src + s * sstride);
     }
+    red[sl][q4] = acc;
+    __syncthreads();
+    if (sl != 0) return;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) acc += red[i][q4];
+    const RowMap rm = map_row(d, hkv, grow);
+    uint16_t* orow = d.out[rm.layer] + ((((int64_t)b * d.Hq + rm.hq) * d.C + rm.qi) * D);
+    uint2 w;
+    w.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    w.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(orow + col) = w;
 }
 
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream)
 {
-    const dim3 grid(total_items), block(64 * kWaves);
+    const dim3 grid(total_items);
     if (multi) {
-        attn_kernel_multi<<<grid, block, 0, stream>>>(p);
+        attn_kernel_multi<<<grid, dim3(256), 0, stream>>>(p);
         return hipGetLastError();
     }
     switch (p.d[0].cfg) {
 #define KVQ_CASE(D_, KB_, VB_) \
     case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
-        attn_kernel<D_, KB_, VB_><<<grid, block, 0, stream>>>(p); break;
+        attn_kernel<D_, KB_, VB_><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); break;
     KVQ_CASE(128, 4, 4) KVQ_CASE(128, 4, 8) KVQ_CASE(128, 8, 4) KVQ_CASE(128, 8, 8)
     KVQ_CASE(256, 4, 4) KVQ_CASE(256, 4, 8) KVQ_CASE(256, 8, 4) KVQ_CASE(256, 8, 8)
     KVQ_CASE(512, 4, 4) KVQ_CASE(512, 4, 8) KVQ_CASE(512, 8, 4) KVQ_CASE(512, 8, 8)
@@ -499,7 +526,8 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t stream)
 {
     int blocks = 0;
     for (int i = 0; i < p.n_desc; ++i)
-        if (p.d[i].S > 1) blocks = p.d[i].comb_begin + p.d[i].B * p.d[i].Hkv * p.d[i].n_rt;
+        if (p.d[i].S > 1)
+            blocks = p.d[i].comb_begin + p.d[i].B * p.d[i].Hkv * p.d[i].n_rt * kRowTile * (p.d[i].D / kCombCols);
     if (blocks == 0) return hipSuccess;
     combine_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();

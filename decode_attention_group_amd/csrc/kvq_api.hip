@@ -148,7 +148,7 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
     int64_t S = (target_wg + items - 1) / items;
-    const int64_t min_steps_per_split = 8;          // two steps per wave
+    const int64_t min_steps_per_split = 4;
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
     const int forced = env_splits();
     if (forced > 0) S = forced;
@@ -182,7 +182,7 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         P.d[i].item_begin = total_items;
         total_items += P.d[i].n_items;
         P.d[i].comb_begin = comb;
-        if (P.d[i].S > 1) comb += P.d[i].B * P.d[i].Hkv * P.d[i].n_rt;
+        if (P.d[i].S > 1) comb += P.d[i].B * P.d[i].Hkv * P.d[i].n_rt * kvq::kRowTile * (P.d[i].D / 64);
         const size_t f = kvq::part_floats(P.d[i]);
         ws = (ws + 255) & ~(size_t)255;
         if (f) ws += f * sizeof(float);
