@@ -8,8 +8,8 @@ kvq_attn_decode_shared).  Inputs are resident in HBM before timing starts.
 
 To read HBM rather than the 256 MB last-level cache, every timed step reads
 one of several identical cache replicas in rotation, so that the rotation
-covers at least --rotate-gib of memory, and a 1 GiB buffer is rewritten
-before each timed region.  The K timed steps are replayed from one HIP graph,
+covers at least --rotate-gib of memory, and a 1 GiB buffer is read before
+each timed region.  The K timed steps are replayed from one HIP graph,
 so host launch overhead does not sit between them.
 
 Output: one JSON line.  `value` is the headline workload's effective KV
@@ -176,11 +176,15 @@ class Runner:
         torch.cuda.synchronize()
         g_step = self._graph(steps, warmup, True)
         g_attn = self._graph(steps, warmup, False)
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        # Evict the last-level cache by reading 1 GiB: a read leaves clean lines,
+        # whereas a write fill would leave dirty ones whose write-back would be
+        # charged to the first timed steps.
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
+        sink = torch.empty(1, dtype=torch.float32, device="cuda")
         stream = torch.cuda.current_stream()
 
         def timed(graph, k):
-            flush.fill_(float(k))
+            torch.sum(flush, dim=0, out=sink[0])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             graph.replay()
@@ -268,6 +272,9 @@ def main():
     ap.add_argument("--only", action="store_true", help="measure only --workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times (reference kernel for "
+                         "scaling the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this library has no multi-GPU path); got --gpus {args.gpus}",
@@ -277,6 +284,15 @@ def main():
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        n = args.copy_probe << 18                       # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4}))
+        return
     head = measure(args.workload, args.steps, args.warmup, args.rotate_gib, not args.no_cpu)
     others = {}
     if not args.only:

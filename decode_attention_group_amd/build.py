@@ -16,6 +16,9 @@ FLAGS = [
     "-fvisibility=hidden", "-ffp-contract=fast",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the softmax and the scale folds read
+    # them, and AGPR copies would cost a VALU move each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -67,14 +67,22 @@ __device__ __forceinline__ RowMap map_row(const AttnDesc& P, int hkv, int grow)
 
 __device__ __forceinline__ int wrap(int slot, int R) { return slot >= R ? slot - R : slot; }
 
-// Registers holding one step's codes and scale|bias words (the prefetch unit).
-template <int D, int KB, int VB>
-struct StepRegs {
-    static constexpr int GPW = Shape<D>::GPW, DTW = Shape<D>::DTW;
-    typename std::conditional<KB == 8, u32x4, u32x2>::type kc[2][GPW];
-    typename std::conditional<VB == 8, u32x2, uint32_t>::type vc[DTW];
-    uint32_t ksb, vsb;
+// Registers holding one step's K codes / V codes and scale|bias words (the
+// prefetch units; K runs one step ahead of V).
+template <int D, int KB>
+struct KRegs {
+    typename std::conditional<KB == 8, u32x4, u32x2>::type kc[2][Shape<D>::GPW];
+    uint32_t sb;
 };
+template <int D, int VB>
+struct VRegs {
+    typename std::conditional<VB == 8, u32x2, uint32_t>::type vc[Shape<D>::DTW];
+    uint32_t sb;
+};
+
+// Largest growth (log2 units) of a row's running max absorbed without
+// rescaling: probabilities are taken against a stale max and may reach 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D, int KB, int VB>
 __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D>& sm)
@@ -83,6 +91,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     constexpr int G = Sh::G, NW = Sh::NW, GPW = Sh::GPW, DTW = Sh::DTW;
     constexpr int KW = D * KB / 32;      // K words per slot
     constexpr int VW = VB / 4;           // V words per (block, d)
+    constexpr int NSLOT = 6 * GPW;       // bias MFMA k-slots in use: {b, s} x 3 parts x groups
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -108,6 +117,9 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const int base = lo & ~(kStep - 1);
     const int j0 = max(lo, base + s * P.split_len);
     const int j1 = min(hi + 1, base + (s + 1) * P.split_len);
+    // keys every row of the tile sees (steps inside need no mask)
+    const int full_lo = max(j0, W > 0 ? len - C + qi_hi - W + 1 : 0);
+    const int full_hi = min(j1 - 1, len - C + qi_lo);
 
     // ---- this lane's query row
     const int grow = row0 + m;
@@ -119,12 +131,12 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     if (!row_ok) { klo = 1; khi = 0; }
 
     // ---- q of this wave's groups as MFMA B operand (fp16, element order matching
-    //      the K code order), and the group sums Q_g for the bias term
+    //      the K code order); Q_g = sum of the group's q for the bias MFMA
     f16x8 qf[GPW][2];
     bf16x8 qb;
-    {
+    auto setup_q = [&]() {
         const uint16_t* qrow = P.q[rm.layer] + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
-        float qsum[GPW];
+        float qpart[3][GPW];
 #pragma unroll
         for (int gi = 0; gi < GPW; ++gi) {
             const int gg = g0 + gi;
@@ -144,7 +156,14 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             float acc = 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc += f[e];
-            qsum[gi] = sum_across_groups(acc);
+            const float Q = sum_across_groups(acc);
+            // Q in three bf16 parts: their sum carries ~24 bits of Q
+            const float q1 = __uint_as_float((uint32_t)f32_to_bf16_rne(Q) << 16);
+            const float q2 = __uint_as_float((uint32_t)f32_to_bf16_rne(Q - q1) << 16);
+            const float q3 = __uint_as_float((uint32_t)f32_to_bf16_rne(Q - q1 - q2) << 16);
+            qpart[0][gi] = q1;
+            qpart[1][gi] = q2;
+            qpart[2][gi] = q3;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int e0 = KB == 8 ? e : nib_order(e);
@@ -152,25 +171,25 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
                 qf[gi][1][e] = (_Float16)f[8 + e0];
             }
         }
-        // k-slots 8*lg + e: Q_g split in three bf16 parts (lg = 0, 1, 2) for group g0+e
-        u32x4 w = 0;
-        if (lg < 3) {
-            uint16_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        // bias k-slot k = (term*3 + part)*GPW + gi: term 0 pairs b with Q, term 1
+        // pairs s with -1024 Q (the K codes enter the MFMA as 1024 + code)
+        uint16_t h[8];
 #pragma unroll
-            for (int gi = 0; gi < GPW; ++gi) {
-                const float q1 = __uint_as_float((uint32_t)f32_to_bf16_rne(qsum[gi]) << 16);
-                const float r1 = qsum[gi] - q1;
-                const float q2 = __uint_as_float((uint32_t)f32_to_bf16_rne(r1) << 16);
-                const float r2 = r1 - q2;
-                h[gi] = lg == 0 ? (uint16_t)(__float_as_uint(q1) >> 16)
-                      : lg == 1 ? (uint16_t)(__float_as_uint(q2) >> 16)
-                                : f32_to_bf16_rne(r2);
-            }
-            w = (u32x4){h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                        h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+        for (int e = 0; e < 8; ++e) {
+            const int k = 8 * lg + e;
+            float v = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < NSLOT; ++kk)
+                if (kk == k) {
+                    const int term = kk / (3 * GPW), part = (kk / GPW) % 3, gi = kk % GPW;
+                    v = term == 0 ? qpart[part][gi] : -1024.0f * qpart[part][gi];
+                }
+            h[e] = (uint16_t)(__float_as_uint(v) >> 16);   // exact: bf16 values times a power of 2
         }
+        const u32x4 w = {h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                         h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
         qb = __builtin_bit_cast(bf16x8, w);
-    }
+    };
 
     const float sl2e = P.scale_log2e;
     f32x4 O[DTW];
@@ -182,31 +201,33 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
     const int st0 = j0 & ~(kStep - 1);
     const int64_t kslot0 = (int64_t)bh * R;
-    const uint32_t* __restrict__ kcodes = P.k_codes;
-    const uint32_t* __restrict__ vcodes = P.v_codes;
+    const uint32_t* __restrict__ kcodes = P.k_codes + kslot0 * KW;
+    const uint32_t* __restrict__ vcodes = P.v_codes + ((int64_t)bh * (R / 8) * D + 64 * g0 + m) * VW;
     // lane -> (key, group) of the scale|bias word it stages each step
     const int sb_key = GPW == 2 ? lane >> 1 : lane & 31;
     const int sb_g = GPW == 2 ? lane & 1 : 0;
     const bool sb_on = GPW == 2 || lane < 32;
+    const uint32_t* __restrict__ ksbp = P.k_sb + kslot0 * G + g0 + sb_g;
+    const uint32_t* __restrict__ vsbp = P.v_sb + kslot0 * G + g0 + sb_g;
 
-    auto load_step = [&](StepRegs<D, KB, VB>& r, int st) {
+    auto load_k = [&](KRegs<D, KB>& r, int st) {
         const int st_mod = st % R;
-        // scale|bias words first: they are the first thing a step consumes
-        const int64_t sbi = (kslot0 + wrap(st_mod + sb_key, R)) * G + g0 + sb_g;
-        r.ksb = P.k_sb[sb_on ? sbi : kslot0 * G];
-        r.vsb = P.v_sb[sb_on ? sbi : kslot0 * G];
+        r.sb = ksbp[sb_on ? wrap(st_mod + sb_key, R) * G : 0];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
-            const uint32_t* krow = kcodes + (kslot0 + wrap(st_mod + kk, R)) * KW;
+            const uint32_t* krow = kcodes + wrap(st_mod + kk, R) * KW;
 #pragma unroll
             for (int gi = 0; gi < GPW; ++gi) {
                 if constexpr (KB == 8) r.kc[t][gi] = *reinterpret_cast<const u32x4*>(krow + (g0 + gi) * 16 + lg * 4);
                 else r.kc[t][gi] = *reinterpret_cast<const u32x2*>(krow + (g0 + gi) * 8 + lg * 2);
             }
         }
-        const int vslot = wrap(st_mod + 8 * lg, R);
-        const uint32_t* vrow = vcodes + (((int64_t)bh * (R / 8) + (vslot >> 3)) * D + 64 * g0 + m) * VW;
+    };
+    auto load_v = [&](VRegs<D, VB>& r, int st) {
+        const int st_mod = st % R;
+        r.sb = vsbp[sb_on ? wrap(st_mod + sb_key, R) * G : 0];
+        const uint32_t* vrow = vcodes + (wrap(st_mod + 8 * lg, R) >> 3) * (D * VW);
 #pragma unroll
         for (int dd = 0; dd < DTW; ++dd) {
             if constexpr (VB == 8) r.vc[dd] = *reinterpret_cast<const u32x2*>(vrow + 16 * dd * VW);
@@ -214,41 +235,43 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     };
 
-    // One step: stage scale|bias, partial scores, exchange, softmax, PV.
-    // `par` alternates the LDS score buffer between consecutive steps.
-    auto compute_step = [&](const StepRegs<D, KB, VB>& cr, int st, int par) {
-        // ---- stage the step's scale|bias words in this wave's LDS region
-        if (sb_on) {
-            sm.ksb[wave][sb_g][sb_key] = cr.ksb;
-            sm.vsb[wave][sb_g][sb_key] = cr.vsb;
-        }
+    // ---- QK of one step: partial S^T over this wave's groups into spart[par].
+    //      Tile t row r holds key 8*(r/4) + 4*t + r%4, so lane group lg ends with
+    //      keys 8*lg .. 8*lg+7.
+    auto qk = [&](const KRegs<D, KB>& kr, int par) {
+        if (sb_on) sm.ksb[wave][sb_g][sb_key] = kr.sb;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- partial S^T over this wave's groups.  Tile t row r holds key
-        //      8*(r/4) + 4*t + r%4, so lane group lg ends with keys 8*lg .. 8*lg+7.
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
             bf16x8 ab;
             {
-                u32x4 w = 0;
-                if (lg < 3) {
-                    uint32_t bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                uint32_t hw[8];
 #pragma unroll
-                    for (int e = 0; e < GPW; ++e) bw[e] = sm.ksb[wave][e][kk] >> 16;
-                    w = (u32x4){bw[0] | (bw[1] << 16), bw[2] | (bw[3] << 16),
-                                bw[4] | (bw[5] << 16), bw[6] | (bw[7] << 16)};
+                for (int e = 0; e < 8; ++e) {
+                    const int k = 8 * lg + e;
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int q = 0; q < NSLOT; ++q)
+                        if (q == k) {
+                            const int term = q / (3 * GPW), gi = q % GPW;
+                            const uint32_t w = sm.ksb[wave][gi][kk];
+                            v = term == 0 ? (w >> 16) : (w & 0xFFFFu);
+                        }
+                    hw[e] = v;
                 }
+                const u32x4 w = {hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
+                                 hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
                 ab = __builtin_bit_cast(bf16x8, w);
             }
             f32x4 sacc = mfma_bf16(ab, qb, (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int gi = 0; gi < GPW; ++gi) {
                 f16x8 a0, a1;
-                if constexpr (KB == 8) codes8x16_to_f16(cr.kc[t][gi], a0, a1);
-                else { a0 = codes4x8_to_f16(cr.kc[t][gi].x); a1 = codes4x8_to_f16(cr.kc[t][gi].y); }
+                if constexpr (KB == 8) codes8x16_to_f16_off(kr.kc[t][gi], a0, a1);
+                else { a0 = codes4x8_to_f16_off(kr.kc[t][gi].x); a1 = codes4x8_to_f16_off(kr.kc[t][gi].y); }
                 f32x4 x = mfma_f16(a0, qf[gi][0], (f32x4){0.f, 0.f, 0.f, 0.f});
                 x = mfma_f16(a1, qf[gi][1], x);
                 const u32x4 sw = *reinterpret_cast<const u32x4*>(&sm.ksb[wave][gi][8 * lg + 4 * t]);
@@ -257,9 +280,12 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             }
             sm.spart[par][wave][t][lane] = sacc;
         }
-        __syncthreads();
+    };
 
-        // ---- full scores (same in every wave) and the online softmax, base 2
+    // ---- full scores of one step (same in every wave, after the barrier) and the
+    //      online softmax in base 2; FULL: every key visible to every row.
+    auto softmax = [&](int st, int par, float (&p)[8], auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         float z[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -268,38 +294,54 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             for (int w = 1; w < NW; ++w) sacc += sm.spart[par][w][t][lane];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = st + 8 * lg + 4 * t + i;
-                z[4 * t + i] = (key >= klo && key <= khi) ? sacc[i] * sl2e : -INFINITY;
+                if constexpr (FULL) {
+                    z[4 * t + i] = sacc[i] * sl2e;
+                } else {
+                    const int key = st + 8 * lg + 4 * t + i;
+                    z[4 * t + i] = (key >= klo && key <= khi) ? sacc[i] * sl2e : -INFINITY;
+                }
             }
         }
         float mloc = z[0];
 #pragma unroll
         for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, z[k]);
-        const float m_new = fmaxf(m_run, max_across_groups(mloc));
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float p[8];
-        float psum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { p[k] = __builtin_amdgcn_exp2f(z[k] - m_use); psum += p[k]; }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__any(alpha != 1.0f)) {
+        const float mt = max_across_groups(mloc);
+        if (__any(mt > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
             for (int dt = 0; dt < DTW; ++dt) O[dt] *= alpha;
             corr *= alpha;
+            l_run *= alpha;
+            m_run = m_new;
         }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            // masked keys come out as exactly 0 (exp2(-inf)); p < 0 flags them for PV
+            const float e = __builtin_amdgcn_exp2f(z[k] - m_use);
+            l_run += e;
+            p[k] = FULL || z[k] != -INFINITY ? e : -1.0f;
+        }
+    };
 
-        // ---- O^T += V^T (P * s_v)^T per group; the bias term of all groups in one MFMA.
-        //      vk: key visible to this lane's query row (B side, per row).  kin: key
-        //      inside the item's range, so its slot holds data (A side, where a row
-        //      is a quantization group and not a query row).
-        bool vk[8], kin[8];
+    // ---- PV of one step: O^T += V^T (P * s_v)^T per group; the bias term of all
+    //      groups in one MFMA.  Per-row visibility is carried by p (< 0: hidden);
+    //      kin: key inside the item's range, so its slot holds data (A side, where
+    //      a row is a quantization group and not a query row).
+    auto pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8], auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        if (sb_on) sm.vsb[wave][sb_g][sb_key] = vr.sb;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        bool kin[8];
+        float pp[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int key = st + 8 * lg + k;
-            vk[k] = z[k] != -INFINITY;
-            kin[k] = key >= j0 && key < j1;
+            kin[k] = FULL || (key >= j0 && key < j1);
+            pp[k] = FULL ? p[k] : fmaxf(p[k], 0.0f);
         }
         {
             f16x8 pb, ac;
@@ -312,7 +354,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             for (int e = 0; e < 8; ++e) {
                 const int k = VB == 8 ? e : nib_order(e);
                 const uint32_t bw = k < 4 ? w0[k & 3] : w1[k & 3];
-                pb[e] = (_Float16)p[k];
+                pb[e] = (_Float16)pp[k];
                 ac[e] = kin[k] ? (_Float16)bf16_hi_to_f32(bw) : (_Float16)0.0f;
             }
             corr = mfma_f16(ac, pb, corr);
@@ -326,34 +368,69 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             for (int e = 0; e < 8; ++e) {
                 const int k = VB == 8 ? e : nib_order(e);
                 const float sv = bf16_lo_to_f32(k < 4 ? s0[k & 3] : s1[k & 3]);
-                bs[e] = vk[k] ? (_Float16)(p[k] * sv) : (_Float16)0.0f;
+                bs[e] = FULL || p[k] >= 0.0f ? (_Float16)(p[k] * sv) : (_Float16)0.0f;
             }
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) {
                 const int dt = 4 * gi + dd;
                 f16x8 a;
-                if constexpr (VB == 8) a = codes8x8_to_f16(cr.vc[dt]);
-                else a = codes4x8_to_f16(cr.vc[dt]);
+                if constexpr (VB == 8) a = codes8x8_to_f16(vr.vc[dt]);
+                else a = codes4x8_to_f16(vr.vc[dt]);
                 O[dt] = mfma_f16(a, bs, O[dt]);
             }
         }
     };
 
-    // Ping-pong between two register sets so the next step's loads stay in
-    // flight while this step computes (a register copy would force a wait).
-    // The loads are issued unconditionally (the step index is clamped, so past
-    // the end the last step is read again and hits L2): a load under a branch
-    // would make the wait counters fall back to waiting for every load.
-    StepRegs<D, KB, VB> ra, rb;
+    auto is_full = [&](int st) { return st >= full_lo && st + kStep - 1 <= full_hi; };
+    auto do_softmax = [&](int st, int par, float (&p)[8]) {
+        if (is_full(st)) softmax(st, par, p, std::true_type{});
+        else softmax(st, par, p, std::false_type{});
+    };
+    auto do_pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8]) {
+        if (is_full(st)) pv(vr, st, p, std::true_type{});
+        else pv(vr, st, p, std::false_type{});
+    };
+
+    // Software pipeline over steps: iteration i runs QK of step i+1 and PV of
+    // step i (independent, so their MFMA and VALU chains interleave), then one
+    // barrier, then the softmax of step i+1.  K codes are loaded two steps
+    // ahead of their QK and V codes one step ahead of their PV, into ping-pong
+    // register sets (no copies: a copy would wait for the load).  Loads are
+    // issued unconditionally with the step index clamped, so the wait counters
+    // stay exact; past the end the last step is read again from L2.
     const int last = max(nsteps - 1, 0);
-    if (nsteps > 0) load_step(ra, st0);
-    for (int si = 0; si < nsteps; si += 2) {
-        const int st = st0 + si * kStep;
-        load_step(rb, st0 + min(si + 1, last) * kStep);
-        compute_step(ra, st, 0);
-        if (si + 1 >= nsteps) break;
-        load_step(ra, st0 + min(si + 2, last) * kStep);
-        compute_step(rb, st + kStep, 1);
+    auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
+    KRegs<D, KB> ka, kb;
+    VRegs<D, VB> va, vb;
+    float p[8];
+    // the first steps' loads go out before q is read and prepared
+    if (nsteps > 0) {
+        load_k(ka, stp(0));
+        load_v(va, stp(0));
+        load_k(kb, stp(1));
+    }
+    setup_q();
+    if (nsteps > 0) {
+        qk(ka, 0);
+        __syncthreads();
+        do_softmax(st0, 0, p);
+    }
+    for (int i = 0; i < nsteps; i += 2) {
+        load_k(ka, stp(i + 2));
+        load_v(vb, stp(i + 1));
+        if (i + 1 < nsteps) qk(kb, 1);
+        do_pv(va, st0 + i * kStep, p);
+        __syncthreads();
+        if (i + 1 >= nsteps) break;
+        do_softmax(st0 + (i + 1) * kStep, 1, p);
+
+        load_k(kb, stp(i + 3));
+        load_v(va, stp(i + 2));
+        if (i + 2 < nsteps) qk(ka, 0);
+        do_pv(vb, st0 + (i + 1) * kStep, p);
+        __syncthreads();
+        if (i + 2 >= nsteps) break;
+        do_softmax(st0 + (i + 2) * kStep, 0, p);
     }
 
     // ---- fold the bias term into O: lane (m, lg) holds corr[group row 4*lg+i][query row m]
@@ -434,14 +511,18 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
 
 // One workgroup per (descriptor, row tile item, row, 64-column chunk):
 // out = sum_s w_s o_s / sum_s w_s l_s, w_s = 2^(m_s - max m).  The 256 threads
-// are 16 column quads x 16 split lanes; each split lane sums every 16th split
-// and the 16 sums meet in LDS.  Splits that saw no key (m_s = -inf) are skipped.
+// are 16 column quads x 16 split lanes.  Each split lane issues the loads of all
+// its splits first, then folds them with a running max, so the partials are
+// read in one round trip; the 16 lanes' results meet in LDS.  Splits that saw
+// no key (m_s = -inf) contribute nothing.
 constexpr int kCombCols = 64;
+constexpr int kCombLanes = 16;
+constexpr int kCombMaxPer = kMaxSplits / kCombLanes;
 
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
 {
-    __shared__ float wts[kMaxSplits];
-    __shared__ f32x4 red[16][16];
+    __shared__ f32x4 red_o[kCombLanes][16];
+    __shared__ float red_m[kCombLanes], red_l[kCombLanes];
     const int bid = blockIdx.x;
     int di = -1;
     for (int i = 0; i < P.n_desc; ++i)
@@ -463,42 +544,65 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
     const float* po = d.part;
     const float* pml = d.part + (size_t)d.B * d.Hkv * d.n_rt * S * kRowTile * D;
     const int tid = threadIdx.x;
-    if (tid < 64) {
-        float M = -INFINITY;
-        for (int s = tid; s < S; s += 64) M = fmaxf(M, pml[(((int64_t)ib * S + s) * kRowTile + r) * 2]);
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float L = 0.0f;
-        for (int s = tid; s < S; s += 64) {
-            const float* ml = pml + (((int64_t)ib * S + s) * kRowTile + r) * 2;
-            const float w = ml[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[0] - M);
-            wts[s] = w;
-            L += w * ml[1];
-        }
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        for (int s = tid; s < S; s += 64) wts[s] *= inv;
-    }
-    __syncthreads();
     const int q4 = tid & 15;           // column quad within the chunk
-    const int sl = tid >> 4;           // split lane
+    const int sl = tid >> 4;           // split lane: splits sl, sl + 16, ...
     const int col = ch * kCombCols + 4 * q4;
-    const float* src = po + (((int64_t)ib * S) * kRowTile + r) * D + col;
     const int64_t sstride = (int64_t)kRowTile * D;
-    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int s = sl; s < S; s += 16) {
-        const float w = wts[s];
-        if (w != 0.0f) acc += w * *reinterpret_cast<const f32x4*>(src + s * sstride);
+    const float* src = po + (((int64_t)ib * S) * kRowTile + r) * D + col;
+    const float* msrc = pml + (((int64_t)ib * S) * kRowTile + r) * 2;
+
+    float ms[kCombMaxPer], ls[kCombMaxPer];
+    f32x4 os[kCombMaxPer];
+#pragma unroll
+    for (int j = 0; j < kCombMaxPer; ++j) {
+        const int s = sl + kCombLanes * j;
+        if (s < S) {
+            const float2 ml = *reinterpret_cast<const float2*>(msrc + (int64_t)s * kRowTile * 2);
+            ms[j] = ml.x;
+            ls[j] = ml.y;
+            os[j] = *reinterpret_cast<const f32x4*>(src + s * sstride);
+        } else {
+            ms[j] = -INFINITY;
+            ls[j] = 0.0f;
+            os[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
     }
-    red[sl][q4] = acc;
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kCombMaxPer; ++j) M = fmaxf(M, ms[j]);
+    float L = 0.0f;
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kCombMaxPer; ++j) {
+        if (ms[j] == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(ms[j] - M);
+        L += w * ls[j];
+        acc += w * os[j];
+    }
+    red_o[sl][q4] = acc;
+    if (q4 == 0) { red_m[sl] = M; red_l[sl] = L; }
     __syncthreads();
     if (sl != 0) return;
+    float Mt = -INFINITY;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) acc += red[i][q4];
+    for (int i = 0; i < kCombLanes; ++i) Mt = fmaxf(Mt, red_m[i]);
+    float Lt = 0.0f;
+    f32x4 ot = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kCombLanes; ++i) {
+        const float mi = red_m[i];
+        if (mi == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(mi - Mt);
+        Lt += w * red_l[i];
+        ot += w * red_o[i][q4];
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    ot *= inv;
     const RowMap rm = map_row(d, hkv, grow);
     uint16_t* orow = d.out[rm.layer] + ((((int64_t)b * d.Hq + rm.hq) * d.C + rm.qi) * D);
     uint2 w;
-    w.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-    w.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    w.x = f32_to_bf16_rne(ot[0]) | ((uint32_t)f32_to_bf16_rne(ot[1]) << 16);
+    w.y = f32_to_bf16_rne(ot[2]) | ((uint32_t)f32_to_bf16_rne(ot[3]) << 16);
     *reinterpret_cast<uint2*>(orow + col) = w;
 }
 

@@ -148,7 +148,7 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
     int64_t S = (target_wg + items - 1) / items;
-    const int64_t min_steps_per_split = 4;
+    const int64_t min_steps_per_split = 1;
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
     const int forced = env_splits();
     if (forced > 0) S = forced;

@@ -50,6 +50,27 @@ __device__ __forceinline__ void codes8x16_to_f16(const u32x4 w, f16x8 &a0, f16x8
     a1 = (f16x8){p4.x, p4.y, p5.x, p5.y, p6.x, p6.y, p7.x, p7.y};
 }
 
+// 16 8-bit codes (4 words) -> two operands of fp16 values 1024 + code (one
+// v_perm_b32 per pair, no subtraction); the caller cancels the offset.
+__device__ __forceinline__ void codes8x16_to_f16_off(const u32x4 w, f16x8 &a0, f16x8 &a1)
+{
+    const uint32_t lo = 0x04010400u, hi = 0x04030402u, c = 0x64646464u;
+    const u32x4 x0 = {__builtin_amdgcn_perm(c, w.x, lo), __builtin_amdgcn_perm(c, w.x, hi),
+                      __builtin_amdgcn_perm(c, w.y, lo), __builtin_amdgcn_perm(c, w.y, hi)};
+    const u32x4 x1 = {__builtin_amdgcn_perm(c, w.z, lo), __builtin_amdgcn_perm(c, w.z, hi),
+                      __builtin_amdgcn_perm(c, w.w, lo), __builtin_amdgcn_perm(c, w.w, hi)};
+    a0 = __builtin_bit_cast(f16x8, x0);
+    a1 = __builtin_bit_cast(f16x8, x1);
+}
+
+// 8 4-bit codes (1 word) -> fp16 values 1024 + code, element order {0,4,1,5,2,6,3,7}.
+__device__ __forceinline__ f16x8 codes4x8_to_f16_off(uint32_t w)
+{
+    const u32x4 x = {(w & 0x000F000Fu) | 0x64006400u, ((w >> 4) & 0x000F000Fu) | 0x64006400u,
+                     ((w >> 8) & 0x000F000Fu) | 0x64006400u, ((w >> 12) & 0x000F000Fu) | 0x64006400u};
+    return __builtin_bit_cast(f16x8, x);
+}
+
 // 8 8-bit codes (2 words) -> one operand of 8 fp16, element order.
 __device__ __forceinline__ f16x8 codes8x8_to_f16(const u32x2 w)
 {
