@@ -65,7 +65,6 @@ __device__ __forceinline__ RowMap map_row(const AttnDesc& P, int hkv, int grow)
     return r;
 }
 
-__device__ __forceinline__ int wrap(int slot, int R) { return slot >= R ? slot - R : slot; }
 
 // Registers holding one step's K codes / V codes and scale|bias words (the
 // prefetch units; K runs one step ahead of V).
@@ -212,11 +211,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
 
     auto load_k = [&](KRegs<D, KB>& r, int st) {
         const int st_mod = st % R;
-        r.sb = ksbp[sb_on ? wrap(st_mod + sb_key, R) * G : 0];
+        r.sb = ksbp[sb_on ? wrap_slot(st_mod + sb_key, R) * G : 0];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
-            const uint32_t* krow = kcodes + wrap(st_mod + kk, R) * KW;
+            const uint32_t* krow = kcodes + wrap_slot(st_mod + kk, R) * KW;
 #pragma unroll
             for (int gi = 0; gi < GPW; ++gi) {
                 if constexpr (KB == 8) r.kc[t][gi] = *reinterpret_cast<const u32x4*>(krow + (g0 + gi) * 16 + lg * 4);
@@ -226,8 +225,8 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     };
     auto load_v = [&](VRegs<D, VB>& r, int st) {
         const int st_mod = st % R;
-        r.sb = vsbp[sb_on ? wrap(st_mod + sb_key, R) * G : 0];
-        const uint32_t* vrow = vcodes + (wrap(st_mod + 8 * lg, R) >> 3) * (D * VW);
+        r.sb = vsbp[sb_on ? wrap_slot(st_mod + sb_key, R) * G : 0];
+        const uint32_t* vrow = vcodes + (wrap_slot(st_mod + 8 * lg, R) >> 3) * (D * VW);
 #pragma unroll
         for (int dd = 0; dd < DTW; ++dd) {
             if constexpr (VB == 8) r.vc[dd] = *reinterpret_cast<const u32x2*>(vrow + 16 * dd * VW);

@@ -299,6 +299,39 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
     return plan_all(rs, n_groups, P, total);
 }
 
+// Prefill with head_dim 256 or 512 runs the prefill kernel: 64 query rows per
+// workgroup share each dequantized key step.  Other head_dims use the decode
+// kernel with per-row positions.
+bool use_prefill_kernel(const kvq_cache* c, int chunk) { return chunk > 1 && c->head_dim >= 256; }
+
+size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
+{
+    std::memset(&P, 0, sizeof(P));
+    P.n_desc = 1;
+    plan_read(r, 1, P.d[0]);                      // shape fields
+    kvq::AttnDesc& d = P.d[0];
+    const kvq_cache* c = r.cache;
+    const int n_rb = (d.n_rows + kvq::kPrefillRows - 1) / kvq::kPrefillRows;
+    int64_t vis = r.max_len;
+    if (c->window > 0)
+        vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kPrefillRows + d.hpk - 1) / d.hpk);
+    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
+    const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
+    const int kTargetWg = 128;     // one 256-thread workgroup on half the CUs before splitting keys
+    int64_t S = (kTargetWg + items - 1) / items;
+    const int forced = env_splits();
+    if (forced > 0) S = forced;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
+    const int64_t steps_per = (steps + S - 1) / S;
+    d.split_len = (int)(steps_per * kvq::kStep);
+    d.S = (int)((steps + steps_per - 1) / steps_per);
+    d.n_items = (int)(items * d.S);
+    d.item_begin = 0;
+    d.comb_begin = 0;
+    total_items = d.n_items;
+    return kvq::part_floats(d) * sizeof(float);
+}
+
 KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t chunk, int32_t max_len)
 {
     if (check_cache(cache, "kvq_prefill_workspace_bytes") != KVQ_OK) return SIZE_MAX;
@@ -306,7 +339,7 @@ KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_h
     ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, chunk};
     kvq::AttnParams P;
     int total = 0;
-    return plan_all(&r, 1, P, total);
+    return use_prefill_kernel(cache, chunk) ? plan_prefill(r, P, total) : plan_all(&r, 1, P, total);
 }
 
 KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
@@ -333,7 +366,21 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, chunk};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
-    return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+    if (!use_prefill_kernel(cache, chunk)) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+    kvq::AttnParams P;
+    int total_items = 0;
+    const size_t need = plan_prefill(r, P, total_items);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
+    bind_workspace(P, workspace);
+    if (trace_on())
+        fprintf(stderr, "[kvq] %s prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d split=%d wg=%d\n",
+                what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].R, P.d[0].W, P.d[0].C, P.d[0].n_rows,
+                P.d[0].S, P.d[0].split_len, total_items);
+    hipError_t e = kvq::launch_prefill(P, total_items, stream);
+    if (e == hipSuccess) e = kvq::launch_combine(P, stream);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
 }
 
 KVQ_API kvq_status kvq_attn_decode_shared(const kvq_shared_group* groups, int32_t n_groups,

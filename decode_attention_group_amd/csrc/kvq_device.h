@@ -16,6 +16,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Slot of a position already reduced to [0, 2R): one conditional subtraction.
+__device__ __forceinline__ int wrap_slot(int slot, int R) { return slot >= R ? slot - R : slot; }
+
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -74,5 +74,9 @@ inline size_t part_floats(const AttnDesc& d)
 hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
+hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);
+
+// Query rows per prefill workgroup (4 waves x 16 rows).
+constexpr int kPrefillRows = 64;
 
 }  // namespace kvq

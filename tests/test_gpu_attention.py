@@ -165,6 +165,10 @@ PREFILL_CASES = [
     (2, 4, 1, 128, 8, 8, 256, 0, 200, 64),
     (1, 8, 2, 256, 4, 8, 1024, 512, 2000, 512),
     (2, 2, 2, 512, 8, 4, 96, 48, 150, 17),
+    (1, 4, 4, 256, 8, 8, 256, 0, 130, 33),      # MHA: 33 rows, last wave of the block idle
+    (3, 16, 2, 512, 4, 8, 512, 256, 700, 70),   # 560 rows per KV head: 9 row blocks, ragged
+    (2, 8, 2, 256, 8, 4, 200, 64, 400, 96),     # ring capacity not a multiple of 32
+    (1, 8, 1, 512, 8, 8, 64, 0, 40, 40),        # whole cache is the chunk, single step
 ]
 
 
@@ -178,6 +182,22 @@ def test_prefill_small(case):
     out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
     torch.cuda.synchronize()
     assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill {case}")
+
+
+@pytest.mark.parametrize("splits", ["1", "3", "7"])
+def test_prefill_split_invariance(splits):
+    B, Hq, Hkv, D, kb, vb, R, W, L, C = (2, 8, 2, 256, 4, 4, 1024, 0, 900, 100)
+    print(f"prefill splits={splits}", flush=True)
+    g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=77)
+    q = small_q_bits(78, (B, Hq, C, D), D ** -0.25)
+    lens = np.array([900, 700], np.int32)            # ragged: batch 1 sees a shorter prefix
+    os.environ["KVQ_SPLITS"] = splits
+    try:
+        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("KVQ_SPLITS", None)
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill splits={splits}")
 
 
 def test_prefill_workload():
