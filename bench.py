@@ -44,6 +44,37 @@ BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode attention effective KV GB/s (% of HBM peak); prefill TFLOP/s"
 
 
+PROFILES = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_sources_sha() -> str:
+    """Hash of the kernel sources, recorded next to the HBM counters they were taken with."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "decode_attention_group_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".h")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None when there are none or the
+    kernel sources changed since they were taken."""
+    try:
+        with open(PROFILES) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256_16") != kernel_sources_sha():
+        return None
+    w = t.get("workloads", {}).get(name)
+    return None if w is None else int(w["bytes_per_launch"])
+
+
 def visible(spec, p):
     lo = max(0, p - spec.window + 1) if spec.window else 0
     return p - lo + 1
@@ -254,7 +285,7 @@ def measure(name, steps, warmup, rotate_gib, with_cpu):
                    roofline={"bound": "hbm", "achieved": round(byts / (attn_ms * 1e-3) / 1e9, 2),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(byts / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5)})
-    res["roofline"]["traffic"] = None
+    res["roofline"]["traffic"] = measured_traffic(name)
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, runner)
     del runner
