@@ -191,7 +191,10 @@ def kvq_prefill_workspace_bytes(cache: KVCache, n_q_heads: int, chunk: int, max_
 def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return workspace
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise KvqError(4, f"workspace of {workspace.numel() * workspace.element_size()} bytes given, "
+                              f"{nbytes} needed")
         return workspace
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 

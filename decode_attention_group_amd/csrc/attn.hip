@@ -55,6 +55,28 @@ struct RowMap {
     int layer, qi, hq;
 };
 
+// (readfirstlane keeps a pointer a scalar value.)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Query / output pointer of each lane's layer.  The 16 rows of a tile cover
+// layers LO..HI (uniform); a short uniform loop loads each of those pointers
+// with a scalar load and selects per lane.  (An unrolled select over all
+// entries is turned by the compiler into a per-lane table lookup: a vector
+// load that delays the q loads, or a private copy in scratch.)
+#define KVQ_LAYER_PTR(T, ARR, LO, HI, LAYER) ([&]() {                              \
+        uint64_t p_ = 0;                                                          \
+        _Pragma("nounroll") for (int l_ = (LO); l_ <= (HI); ++l_) {               \
+            const uint64_t a_ = uniform_u64(reinterpret_cast<uint64_t>((ARR)[l_])); \
+            if ((LAYER) == l_) p_ = a_;                                           \
+        }                                                                         \
+        return as_global(reinterpret_cast<T*>(p_));                              \
+    }())
+
 __device__ __forceinline__ RowMap map_row(const AttnDesc& P, int hkv, int grow)
 {
     RowMap r;
@@ -102,48 +124,64 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const int rt = (idx / S) % P.n_rt;
     const int bh = idx / (S * P.n_rt);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
-    const int len = min(max(P.len[b], 0), P.max_len);
     const int R = P.R, W = P.W, C = P.C;
+    // len[b] is read in flight: the ranges below are first taken for the
+    // common case len == max_len, so the first code loads go out without
+    // waiting for it, and are reissued when it differs.
+    // (a vector load: a scalar one would share its wait counter with the
+    // kernel-argument loads and be waited for before the first code loads)
+    int opaque_zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+    const int len_lane = as_global(P.len)[b + opaque_zero];
 
-    // ---- key range of this work item
+    // ---- key range of this work item, and of this lane's query row
     const int row0 = rt * kRowTile;
     const int last_row = min(row0 + kRowTile, P.n_rows) - 1;
     const int qi_lo = C == 1 ? 0 : row0 / P.hpk;
     const int qi_hi = C == 1 ? 0 : last_row / P.hpk;
-    int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
-    lo = max(lo, max(0, len - R));
-    const int hi = len - C + qi_hi;
-    const int base = lo & ~(kStep - 1);
-    const int j0 = max(lo, base + s * P.split_len);
-    const int j1 = min(hi + 1, base + (s + 1) * P.split_len);
-    // keys every row of the tile sees (steps inside need no mask)
-    const int full_lo = max(j0, W > 0 ? len - C + qi_hi - W + 1 : 0);
-    const int full_hi = min(j1 - 1, len - C + qi_lo);
-
-    // ---- this lane's query row
     const int grow = row0 + m;
     const bool row_ok = grow < P.n_rows;
     const RowMap rm = map_row(P, hkv, row_ok ? grow : row0);
-    const int p_row = len - C + rm.qi;
-    int klo = max(j0, W > 0 ? p_row - W + 1 : 0);
-    int khi = min(j1 - 1, p_row);
-    if (!row_ok) { klo = 1; khi = 0; }
+    const int lay_lo = map_row(P, hkv, row0).layer, lay_hi = map_row(P, hkv, last_row).layer;
+    int j0, j1, full_lo, full_hi, klo, khi;
+    auto ranges = [&](int len) {
+        int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
+        lo = max(lo, max(0, len - R));
+        const int hi = len - C + qi_hi;
+        const int base = lo & ~(kStep - 1);
+        j0 = max(lo, base + s * P.split_len);
+        j1 = min(hi + 1, base + (s + 1) * P.split_len);
+        // keys every row of the tile sees (steps inside need no mask)
+        full_lo = max(j0, W > 0 ? len - C + qi_hi - W + 1 : 0);
+        full_hi = min(j1 - 1, len - C + qi_lo);
+        const int p_row = len - C + rm.qi;
+        klo = max(j0, W > 0 ? p_row - W + 1 : 0);
+        khi = min(j1 - 1, p_row);
+        if (!row_ok) { klo = 1; khi = 0; }
+    };
+    ranges(P.max_len);
 
     // ---- q of this wave's groups as MFMA B operand (fp16, element order matching
     //      the K code order); Q_g = sum of the group's q for the bias MFMA
     f16x8 qf[GPW][2];
     bf16x8 qb;
+    // q loads are unconditional (a lane past the last row reads row 0 of the
+    // tile and zeroes it afterwards), so no branch forces an early wait.
+    u32x4 qraw[GPW][2];
+    auto load_q = [&]() {
+        const uint16_t* qrow = KVQ_LAYER_PTR(const uint16_t, P.q, lay_lo, lay_hi, rm.layer) + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+            qraw[gi][0] = *reinterpret_cast<const u32x4*>(qrow + (g0 + gi) * 64 + lg * 16);
+            qraw[gi][1] = *reinterpret_cast<const u32x4*>(qrow + (g0 + gi) * 64 + lg * 16 + 8);
+        }
+    };
     auto setup_q = [&]() {
-        const uint16_t* qrow = P.q[rm.layer] + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
         float qpart[3][GPW];
 #pragma unroll
         for (int gi = 0; gi < GPW; ++gi) {
-            const int gg = g0 + gi;
-            u32x4 u0 = 0, u1 = 0;
-            if (row_ok) {
-                u0 = *reinterpret_cast<const u32x4*>(qrow + gg * 64 + lg * 16);
-                u1 = *reinterpret_cast<const u32x4*>(qrow + gg * 64 + lg * 16 + 8);
-            }
+            const u32x4 u0 = row_ok ? qraw[gi][0] : (u32x4)0;
+            const u32x4 u1 = row_ok ? qraw[gi][1] : (u32x4)0;
             float f[16];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -197,17 +235,17 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     f32x4 corr = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
-    const int st0 = j0 & ~(kStep - 1);
+    int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
+    int st0 = j0 & ~(kStep - 1);
     const int64_t kslot0 = (int64_t)bh * R;
-    const uint32_t* __restrict__ kcodes = P.k_codes + kslot0 * KW;
-    const uint32_t* __restrict__ vcodes = P.v_codes + ((int64_t)bh * (R / 8) * D + 64 * g0 + m) * VW;
+    const uint32_t* __restrict__ kcodes = as_global(P.k_codes) + kslot0 * KW;
+    const uint32_t* __restrict__ vcodes = as_global(P.v_codes) + ((int64_t)bh * (R / 8) * D + 64 * g0 + m) * VW;
     // lane -> (key, group) of the scale|bias word it stages each step
     const int sb_key = GPW == 2 ? lane >> 1 : lane & 31;
     const int sb_g = GPW == 2 ? lane & 1 : 0;
     const bool sb_on = GPW == 2 || lane < 32;
-    const uint32_t* __restrict__ ksbp = P.k_sb + kslot0 * G + g0 + sb_g;
-    const uint32_t* __restrict__ vsbp = P.v_sb + kslot0 * G + g0 + sb_g;
+    const uint32_t* __restrict__ ksbp = as_global(P.k_sb) + kslot0 * G + g0 + sb_g;
+    const uint32_t* __restrict__ vsbp = as_global(P.v_sb) + kslot0 * G + g0 + sb_g;
 
     auto load_k = [&](KRegs<D, KB>& r, int st) {
         const int st_mod = st % R;
@@ -397,16 +435,29 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     // register sets (no copies: a copy would wait for the load).  Loads are
     // issued unconditionally with the step index clamped, so the wait counters
     // stay exact; past the end the last step is read again from L2.
-    const int last = max(nsteps - 1, 0);
+    int last = max(nsteps - 1, 0);
     auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
     KRegs<D, KB> ka, kb;
     VRegs<D, VB> va, vb;
     float p[8];
-    // the first steps' loads go out before q is read and prepared
-    if (nsteps > 0) {
-        load_k(ka, stp(0));
-        load_v(va, stp(0));
-        load_k(kb, stp(1));
+    // q and the first steps' codes go out together, before len[b] is known
+    // (unconditional: a branch around loads would make every later wait a full one;
+    // with no step the clamped index still names slots inside the cache)
+    load_q();
+    load_k(ka, stp(0));
+    load_v(va, stp(0));
+    load_k(kb, stp(1));
+    const int len_act = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
+    if (len_act != P.max_len) {
+        ranges(len_act);
+        nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
+        st0 = j0 & ~(kStep - 1);
+        last = max(nsteps - 1, 0);
+        if (nsteps > 0) {
+            load_k(ka, stp(0));
+            load_v(va, stp(0));
+            load_k(kb, stp(1));
+        }
     }
     setup_q();
     if (nsteps > 0) {
@@ -440,11 +491,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) O[4 * gi + dd] += c;
     }
-    if (!row_ok) return;
     const int dcol = 64 * g0 + 4 * lg;   // + 16 * dt + i
     if (S == 1) {
+        if (!row_ok) return;
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        uint16_t* orow = P.out[rm.layer] + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
+        uint16_t* orow = KVQ_LAYER_PTR(uint16_t, P.out, lay_lo, lay_hi, rm.layer) + ((((int64_t)b * P.Hq + rm.hq) * C + rm.qi) * D);
 #pragma unroll
         for (int dt = 0; dt < DTW; ++dt) {
             const f32x4 o = O[dt] * inv;
@@ -453,17 +504,18 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             w.y = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
             *reinterpret_cast<uint2*>(orow + dcol + 16 * dt) = w;
         }
-    } else {
-        const int64_t ib = (int64_t)bh * P.n_rt + rt;
-        const int64_t prow = (ib * S + s) * kRowTile + m;
-        float* po = P.part + prow * D;
+        return;
+    }
+    if (!row_ok) return;
+    const int64_t ib = (int64_t)bh * P.n_rt + rt;
+    const int64_t prow = (ib * S + s) * kRowTile + m;
+    float* po = as_global(P.part) + prow * D;
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
-        if (wave == 0 && lg == 0) {
-            float* pml = P.part + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
-            pml[0] = m_run;
-            pml[1] = L;
-        }
+    for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
+    if (wave == 0 && lg == 0) {
+        float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
+        pml[0] = m_run;
+        pml[1] = L;
     }
 }
 
@@ -474,13 +526,19 @@ __device__ __forceinline__ int find_desc(const AttnParams& P, int bid)
     return di;
 }
 
-template <int D, int KB, int VB>
+// ONE: a single descriptor, so every field sits at a constant offset and the
+// kernel-argument loads issue together instead of after a descriptor search.
+template <int D, int KB, int VB, bool ONE>
 __global__ __launch_bounds__(64 * Shape<D>::NW) void attn_kernel(AttnParams P)
 {
     __shared__ AttnSmem<D> sm;
     const int bid = blockIdx.x;
-    const int di = find_desc(P, bid);
-    attn_body<D, KB, VB>(P.d[di], bid - P.d[di].item_begin, sm);
+    if constexpr (ONE) {
+        attn_body<D, KB, VB>(P.d[0], bid, sm);
+    } else {
+        const int di = find_desc(P, bid);
+        attn_body<D, KB, VB>(P.d[di], bid - P.d[di].item_begin, sm);
+    }
 }
 
 // One launch over descriptors of different configurations: the Gemma 4 decode
@@ -490,7 +548,7 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
     // One LDS block sized for head_dim 512; the head_dim 256 bodies use a prefix of it.
     static_assert(sizeof(AttnSmem<256>) <= sizeof(AttnSmem<512>), "LDS reuse");
     __shared__ AttnSmem<512> sm;
-    AttnSmem<256>& sm256 = *reinterpret_cast<AttnSmem<256>*>(&sm);
+    AttnSmem<256>& sm256 = *(AttnSmem<256>*)(__attribute__((address_space(3))) AttnSmem<256>*)(&sm);
     const int bid = blockIdx.x;
     const int di = find_desc(P, bid);
     const AttnDesc& d = P.d[di];
@@ -540,8 +598,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
     const int b = bh / d.Hkv, hkv = bh - b * d.Hkv;
     const int grow = rt * kRowTile + r;
     if (grow >= d.n_rows) return;
-    const float* po = d.part;
-    const float* pml = d.part + (size_t)d.B * d.Hkv * d.n_rt * S * kRowTile * D;
+    const float* po = as_global(d.part);
+    const float* pml = as_global(d.part) + (size_t)d.B * d.Hkv * d.n_rt * S * kRowTile * D;
     const int tid = threadIdx.x;
     const int q4 = tid & 15;           // column quad within the chunk
     const int sl = tid >> 4;           // split lane: splits sl, sl + 16, ...
@@ -598,7 +656,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
     const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
     ot *= inv;
     const RowMap rm = map_row(d, hkv, grow);
-    uint16_t* orow = d.out[rm.layer] + ((((int64_t)b * d.Hq + rm.hq) * d.C + rm.qi) * D);
+    uint16_t* orow = as_global(d.out[rm.layer]) + ((((int64_t)b * d.Hq + rm.hq) * d.C + rm.qi) * D);
     uint2 w;
     w.x = f32_to_bf16_rne(ot[0]) | ((uint32_t)f32_to_bf16_rne(ot[1]) << 16);
     w.y = f32_to_bf16_rne(ot[2]) | ((uint32_t)f32_to_bf16_rne(ot[3]) << 16);
@@ -615,7 +673,9 @@ hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStre
     switch (p.d[0].cfg) {
 #define KVQ_CASE(D_, KB_, VB_) \
     case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
-        attn_kernel<D_, KB_, VB_><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); break;
+        if (p.n_desc == 1) attn_kernel<D_, KB_, VB_, true><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
+        else attn_kernel<D_, KB_, VB_, false><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
+        break;
     KVQ_CASE(128, 4, 4) KVQ_CASE(128, 4, 8) KVQ_CASE(128, 8, 4) KVQ_CASE(128, 8, 8)
     KVQ_CASE(256, 4, 4) KVQ_CASE(256, 4, 8) KVQ_CASE(256, 8, 4) KVQ_CASE(256, 8, 8)
     KVQ_CASE(512, 4, 4) KVQ_CASE(512, 4, 8) KVQ_CASE(512, 8, 4) KVQ_CASE(512, 8, 8)

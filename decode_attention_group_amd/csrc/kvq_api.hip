@@ -135,6 +135,7 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     d.max_len = r.max_len;
     d.hpk = r.Hq / c->n_kv_heads;
     d.n_rows = (r.C == 1 ? r.n_layers : r.C) * d.hpk;
+    d.n_layers = r.C == 1 ? r.n_layers : 1;
     d.n_rt = (d.n_rows + kvq::kRowTile - 1) / kvq::kRowTile;
     d.scale_log2e = r.scale * kvq::kLog2e;
     d.cfg = kvq::cfg_id(c->head_dim, c->k_bits, c->v_bits);
@@ -178,12 +179,13 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
     size_t ws = 0;
     for (int i = 0; i < n; ++i) {
         const int target = std::max(1, (int)std::lround(kTargetWg * (total > 0 ? bytes[i] / total : 1.0)));
-        plan_read(rs[i], target, P.d[i]);
-        P.d[i].item_begin = total_items;
-        total_items += P.d[i].n_items;
-        P.d[i].comb_begin = comb;
-        if (P.d[i].S > 1) comb += P.d[i].B * P.d[i].Hkv * P.d[i].n_rt * kvq::kRowTile * (P.d[i].D / 64);
-        const size_t f = kvq::part_floats(P.d[i]);
+        kvq::AttnDesc& d = P.d[i];
+        plan_read(rs[i], target, d);
+        d.item_begin = total_items;
+        total_items += d.n_items;
+        d.comb_begin = comb;
+        if (d.S > 1) comb += d.B * d.Hkv * d.n_rt * kvq::kRowTile * (d.D / 64);
+        const size_t f = kvq::part_floats(d);
         ws = (ws + 255) & ~(size_t)255;
         if (f) ws += f * sizeof(float);
     }

@@ -16,6 +16,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Tag a pointer as global memory.  Pointers read from a kernel-argument array
+// at a run-time index lose their address space; accesses through them would be
+// flat_* instructions, which count against the LDS wait counter as well and
+// so serialize LDS reads behind in-flight global loads.
+template <class T>
+__device__ __forceinline__ T* as_global(T* p)
+{
+    using GT = __attribute__((address_space(1))) T;
+    return (T*)reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Slot of a position already reduced to [0, 2R): one conditional subtraction.
 __device__ __forceinline__ int wrap_slot(int slot, int R) { return slot >= R ? slot - R : slot; }
 

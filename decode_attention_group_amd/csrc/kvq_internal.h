@@ -43,6 +43,7 @@ struct AttnDesc {
     int32_t B, Hkv, Hq, R, W, C, D;
     int32_t max_len;        // len[b] is clamped to [0, max_len]
     int32_t hpk, n_rows, n_rt;
+    int32_t n_layers;       // layers whose queries share the read (1 for prefill)
     int32_t S, split_len;   // splits per (b, kv head, row tile) and keys per split
     int32_t item_begin;     // first workgroup of this descriptor
     int32_t n_items;        // B * Hkv * n_rt * S

@@ -94,6 +94,12 @@ def test_decode_split_invariance_and_determinism():
         os.environ.pop("KVQ_SPLITS", None)
     torch.cuda.synchronize()
     assert torch.equal(outs[-1], again)                      # same plan: bitwise
+    os.environ["KVQ_SPLITS"] = "3"
+    try:
+        again3 = kvq.kvq_attn_decode(g, q, lens, L)
+    finally:
+        os.environ.pop("KVQ_SPLITS", None)
+    assert torch.equal(outs[1], again3)
     ref = o.attend(small_q_bits(6, (B, Hq, D), 0.21)[:, :, None], np.full(B, L, np.int32))[:, :, 0]
     for x in outs:
         assert_close(torch_bf16_to_f64(x), ref, "split")
@@ -113,6 +119,37 @@ def test_decode_workload(name):
     ref = o.attend(q, lens)[:, :, 0]
     mx, mean = assert_close(torch_bf16_to_f64(out), ref, name)
     print(f"{name}: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
+def test_workspace_reuse_across_calls():
+    """One workspace, never cleared, through split decodes, split prefills and
+    shared decodes of different plans: every result matches the oracle."""
+    B, Hkv, D, R, W, L = 2, 2, 256, 1024, 512, 900
+    g, o = make_pair(B, Hkv, D, 4, 8, R, W, L, seed=91)
+    lens_np = np.full(B, L, np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    ws = torch.full((64 << 20,), 0xA5, dtype=torch.uint8, device="cuda")   # stale bytes, never cleared
+    qd = small_q_bits(92, (B, 8, 1, D), 0.25)
+    qp = small_q_bits(93, (B, 8, 64, D), 0.25)
+    ref_d = o.attend(qd, lens_np)[:, :, 0]
+    ref_p = o.attend(qp, lens_np)
+    try:
+        for splits in ("4", "17", "2", "9"):
+            os.environ["KVQ_SPLITS"] = splits
+            print(f"reuse splits={splits}", flush=True)
+            out = kvq.kvq_attn_decode(g, q_dev(qd[:, :, 0].copy()), lens, L, workspace=ws)
+            torch.cuda.synchronize()
+            assert_close(torch_bf16_to_f64(out), ref_d, f"decode splits={splits}")
+            out = kvq.kvq_attn_prefill_chunk(g, q_dev(qp), lens, L, workspace=ws)
+            torch.cuda.synchronize()
+            assert_close(torch_bf16_to_f64(out), ref_p, f"prefill splits={splits}")
+            outs = kvq.kvq_attn_decode_shared([kvq.SharedGroup(g, [q_dev(qd[:, :, 0].copy())] * 2, lens, L)],
+                                              workspace=ws)
+            torch.cuda.synchronize()
+            for x in outs[0]:
+                assert_close(torch_bf16_to_f64(x), ref_d, f"shared splits={splits}")
+    finally:
+        os.environ.pop("KVQ_SPLITS", None)
 
 
 def test_shared_equals_separate_small():
