@@ -301,10 +301,19 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
     return plan_all(rs, n_groups, P, total);
 }
 
-// Prefill with head_dim 256 or 512 runs the prefill kernel: 64 query rows per
-// workgroup share each dequantized key step.  Other head_dims use the decode
-// kernel with per-row positions.
+// Prefill with head_dim 256 or 512 runs the band dequant + prefill kernels (the
+// chunk's key band dequantized once to bf16 in the workspace, then 64 query
+// rows per workgroup).  Other head_dims use the decode kernel with per-row
+// positions.
 bool use_prefill_kernel(const kvq_cache* c, int chunk) { return chunk > 1 && c->head_dim >= 256; }
+
+// Band positions per (b, kv head): every position a query of the chunk can see,
+// from a step-aligned start.
+int64_t band_positions(const kvq_cache* c, int chunk, int max_len)
+{
+    const int64_t span = c->window > 0 ? std::min<int64_t>((int64_t)c->window + chunk - 1, max_len) : max_len;
+    return (span + 2 * kvq::kStep - 1) / kvq::kStep * kvq::kStep;
+}
 
 size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
 {
@@ -330,8 +339,21 @@ size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
     d.n_items = (int)(items * d.S);
     d.item_begin = 0;
     d.comb_begin = 0;
+    d.nk = (int)band_positions(c, r.C, r.max_len);
     total_items = d.n_items;
-    return kvq::part_floats(d) * sizeof(float);
+    // workspace: split partials, then the band tiles (K and V, bf16; four spare
+    // tiles per sequence and KV head that a final prefetch may read)
+    const size_t part = (kvq::part_floats(d) * sizeof(float) + 255) & ~(size_t)255;
+    return part + (size_t)d.B * d.Hkv * (d.nk + 4 * kvq::kStep) * d.D * 2 * sizeof(uint16_t);
+}
+
+void bind_prefill_workspace(kvq::AttnParams& P, void* workspace)
+{
+    kvq::AttnDesc& d = P.d[0];
+    char* base = static_cast<char*>(workspace);
+    const size_t part = (kvq::part_floats(d) * sizeof(float) + 255) & ~(size_t)255;
+    d.part = kvq::part_floats(d) ? reinterpret_cast<float*>(base) : nullptr;
+    d.band = reinterpret_cast<uint16_t*>(base + part);
 }
 
 KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t chunk, int32_t max_len)
@@ -374,11 +396,11 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     const size_t need = plan_prefill(r, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
-    bind_workspace(P, workspace);
+    bind_prefill_workspace(P, workspace);
     if (trace_on())
-        fprintf(stderr, "[kvq] %s prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d split=%d wg=%d\n",
+        fprintf(stderr, "[kvq] %s prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d split=%d wg=%d band=%d\n",
                 what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].R, P.d[0].W, P.d[0].C, P.d[0].n_rows,
-                P.d[0].S, P.d[0].split_len, total_items);
+                P.d[0].S, P.d[0].split_len, total_items, P.d[0].nk);
     hipError_t e = kvq::launch_prefill(P, total_items, stream);
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -40,6 +40,9 @@ struct AttnDesc {
     uint16_t* out[KVQ_MAX_SHARED_LAYERS];
     const int32_t* len;
     float* part;            // split partials (null when S == 1)
+    uint16_t* band;         // prefill: dequantized band tiles, bf16 [B][Hkv][nk/32][64*D] (the
+                            // LDS image of each 32-key step: K rows, then V^T rows, swizzled)
+    int32_t nk;             // prefill: band positions held per (b, kv head), a multiple of 32
     int32_t B, Hkv, Hq, R, W, C, D;
     int32_t max_len;        // len[b] is clamped to [0, max_len]
     int32_t hpk, n_rows, n_rt;

@@ -4,20 +4,29 @@
 // diff, gemma4/model.ts: a prompt chunk's tokens are appended to the cache and
 // its queries then attend the cache read -- causal inside the chunk, windowed
 // on sliding layers): for query i of a chunk of C, at position p = len - C + i,
-// softmax(scale * q . khat_j) over max(0, p-W+1) <= j <= p, times vhat_j.
+// softmax(scale * q . khat_j) over max(0, p-W+1, len-R) <= j <= p, times vhat_j.
 //
-// Unlike decode, many query rows share every key here (chunk queries times the
-// query heads of one KV head), so each 32-key step is dequantized once into LDS
-// and read by all of a workgroup's rows:
-//   * the 256 threads dequantize the step's K (token-major) and V (d-major) to
-//     fp16, x = code * scale + bias in one packed fp16 FMA per value pair;
-//   * each of the 4 waves owns 16 query rows and runs S^T = Khat Q^T and
-//     O^T = Vhat^T P^T on 16x16x32 fp16 MFMA from LDS, with the same online
-//     softmax (base 2, lazy rescale) as the decode kernel.
-// Codes and scale|bias words are fetched two and three steps ahead; LDS holds
-// two steps; one barrier per step.  Rows follow the decode layout
-// (row = query * (Hq/Hkv) + head), so split partials, if any, go through the
-// same combine kernel.
+// Unlike decode, every key of the chunk's band is read by many query rows (the
+// chunk's queries times the query heads of its KV head), so it is dequantized
+// once per call and the attention itself is a plain bf16 flash attention:
+//   band_dequant_kernel: for each (sequence, KV head), the positions any query
+//     of the chunk can see -- the band [base0, len), base0 = that lowest
+//     position rounded down to 32 -- dequantized x = code * scale + bias in
+//     fp32, rounded to bf16, into the workspace as one tile per 32-key step,
+//     laid out exactly as the attention kernel wants it in LDS: the step's 32 K
+//     rows (in MFMA row order) and then its D V^T rows (keys contiguous per
+//     element), 16-byte chunks XOR-swizzled so the MFMA operand reads hit
+//     distinct banks.  Band positions outside what the chunk can see are zeros.
+//   prefill_kernel: one workgroup of 4 waves per (sequence, KV head, 64 query
+//     rows, split).  Tiles are copied global -> LDS with LDS DMA (no register
+//     staging) one round ahead of their use.  Each wave owns RT row tiles of
+//     16 rows, so every K / V^T operand read from LDS feeds RT MFMAs (LDS
+//     bandwidth bounds the one-tile-per-wave layout); the NG wave groups take
+//     alternate steps and merge in LDS at the end.  S^T = K Q^T and
+//     O^T = V^T P^T run on 16x16x32 bf16 MFMA with an online softmax in base 2
+//     (lazy rescale: the running max may trail the true one by up to 2^8).
+// Rows follow the decode layout (row = query * (Hq/Hkv) + head), so split
+// partials, if any, go through the same combine kernel.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -28,58 +37,197 @@ namespace kvq {
 constexpr int kPfWaves = 4;
 constexpr int kPfRows = kPfWaves * kRowTile;   // query rows per workgroup
 constexpr float kPfRescaleSlack = 8.0f;
+// Band tiles kept per (sequence, KV head): the band's steps plus kBandPad more,
+// so a round past the last step may copy past the band without a bounds check
+// (those tiles are never computed on).
+constexpr int kBandPad = 4;
 
-template <int D>
-struct __attribute__((aligned(16))) PfSmem {
-    static constexpr int G = D / 64;
-    // K rows of a step in MFMA order: LDS row 16*t + r holds key 8*(r/4) + 4*t + r%4,
-    // so the 16 rows one MFMA tile reads are consecutive; the row stride is
-    // 4 dwords past a multiple of 64 banks, so those 16 reads hit distinct banks.
-    _Float16 kh[2][kStep][D + 8];
-    // V^T rows: vt[d][8*blk + e] holds key 8*blk + (e for 8-bit V, nibble order
-    // {0,4,1,5,2,6,3,7} for 4-bit V); 80-byte stride, conflict-free 16-lane reads.
-    _Float16 vt[2][D][kStep + 8];
-    uint16_t ks[2][G][kStep], kb[2][G][kStep];   // fp16 K scale / bias, natural key order
-    uint16_t vs[2][G][kStep], vb[2][G][kStep];   // fp16 V scale / bias, V^T element order
-};
-
-template <int D, int KB, int VB>
-struct PfCodes {
-    // K: thread -> (key t/8, head_dim chunk t%8 of D/8 values); V: thread -> d (and d + 256)
-    static constexpr int KWT = D / 8 * KB / 32;          // K words per thread
-    static constexpr int VD = D / 256;                    // head_dim columns per thread
-    static constexpr int VWT = VD * 4 * (VB / 4);         // V words per thread (4 blocks of 8 keys)
-    uint32_t k[KWT];
-    uint32_t v[VWT];
-};
-
-__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
-
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f)
+// Lowest position any query of the chunk sees; the band starts there rounded
+// down to a step.  The two kernels and the host sizing agree on this.
+__device__ __forceinline__ int band_lo(int len, int C, int W, int R)
 {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
+    const int lo = W > 0 ? len - C - W + 1 : 0;
+    return max(lo, max(0, len - R));
+}
+
+// Two fp32 values to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Tile image of one 32-key step, in 16-byte chunks (8 bf16): the K part, 32 rows
+// of D/8 chunks in MFMA row order (k_row), chunk c of a row's elements stored at
+// position c ^ (row % 16); then the V^T part, D rows of 4 chunks (keys 8c ..
+// 8c+7), chunk c of row d stored at position c ^ ((d / 4) % 4).
+// MFMA reads of 16 rows at one logical chunk then touch 16 distinct chunk
+// positions modulo 16, i.e. distinct banks.
+template <int D> constexpr int tile_elems() { return 64 * D; }     // bf16 per step tile
+// LDS row of key k within a step (row 16*t + r holds key 8*(r/4) + 4*t + r%4)
+__device__ __forceinline__ int k_row(int key) { return 16 * ((key >> 2) & 1) + 4 * (key >> 3) + (key & 3); }
+template <int D>
+__device__ __forceinline__ int k_chunk_pos(int row, int c) { return row * (D / 8) + (c ^ (row & 15)); }
+template <int D>
+__device__ __forceinline__ int v_chunk_pos(int d, int c) { return 4 * D + d * 4 + (c ^ ((d >> 2) & 3)); }
+
+// ---------------------------------------------------------------------------
+// Band dequantization.  Grid (band steps, Hkv, B), 256 threads; one 32-key
+// step per workgroup.  K: thread -> (key tid/8, D/8 elements); V: thread ->
+// element d (and d + 256), 32 keys.
+template <int D, int KB, int VB>
+__global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
+{
+    constexpr int G = D / 64;
+    constexpr int KW = D * KB / 32;          // K code words per slot
+    constexpr int VW = VB / 4;               // V code words per (block, d)
+    constexpr int KE = D / 8;                // K elements per thread
+    __shared__ uint32_t vsb[kStep][G];       // V scale|bias words of the step
+    const int tid = threadIdx.x;
+    const int step = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    const int bh = b * P.Hkv + hkv;
+    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
+    const int R = P.R;
+    const int vis_lo = band_lo(len, P.C, P.W, R);
+    const int base0 = vis_lo & ~(kStep - 1);
+    const int p0 = base0 + step * kStep;
+    if (p0 >= len) return;                   // past every query: never read
+    const int64_t kslot0 = (int64_t)bh * R;
+
+    // Every load is issued before any store (stores in between would order
+    // the loads behind them): the V scale|bias words to LDS, then the K codes
+    // and scale|bias word and the V codes to registers.
+    for (int i = tid; i < kStep * G; i += 256) {
+        const int key = i / G, g = i % G;
+        vsb[key][g] = as_global(P.v_sb)[(kslot0 + (p0 + key) % R) * G + g];
+    }
+    const int key = tid >> 3, ch = tid & 7;              // K: key tid/8, elements [KE*(tid%8), +KE)
+    const int kpos = p0 + key;
+    const bool kok = kpos >= vis_lo && kpos < len;
+    const int64_t kslot = kslot0 + kpos % R;
+    constexpr int KWT = KE * KB / 32;                     // K code words per thread
+    uint32_t kw[KWT];
+    {
+        const uint32_t* src = as_global(P.k_codes) + kslot * KW + ch * KWT;
+#pragma unroll
+        for (int w = 0; w < KWT; w += 4) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(src + w);
+            kw[w] = x.x; kw[w + 1] = x.y; kw[w + 2] = x.z; kw[w + 3] = x.w;
+        }
+    }
+    const uint32_t ksbw = as_global(P.k_sb)[kslot * G + ch * KE / 64];
+    constexpr int VD = (D + 255) / 256;                   // elements d per thread
+    uint32_t vw[VD][4][VW];
+#pragma unroll
+    for (int dd = 0; dd < VD; ++dd)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int slot8 = (p0 + 8 * blk) % R;            // a multiple of 8
+            const uint32_t* src = as_global(P.v_codes) + (((int64_t)bh * (R / 8) + slot8 / 8) * D + tid + 256 * dd) * VW;
+#pragma unroll
+            for (int w = 0; w < VW; ++w) vw[dd][blk][w] = src[w];
+        }
+
+    {   // K
+        const float sc = bf16_lo_to_f32(ksbw), bi = bf16_hi_to_f32(ksbw);
+        uint16_t* tile = as_global(P.band) + ((int64_t)bh * (P.nk / kStep + kBandPad) + step) * tile_elems<D>();
+        const int row = k_row(key);
+#pragma unroll
+        for (int e0 = 0; e0 < KE; e0 += 8) {              // 8 elements: one 16-byte chunk
+            uint16_t* dst = tile + 8 * k_chunk_pos<D>(row, (ch * KE + e0) / 8);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ei = e0 + e;
+                const uint32_t c = KB == 8 ? (kw[ei >> 2] >> (8 * (ei & 3))) & 0xFFu : (kw[ei >> 3] >> (4 * (ei & 7))) & 0xFu;
+                x[e] = kok ? __builtin_fmaf((float)c, sc, bi) : 0.0f;
+            }
+            const u32x4 o = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3]),
+                             bf16x2_rne(x[4], x[5]), bf16x2_rne(x[6], x[7])};
+            *reinterpret_cast<u32x4*>(dst) = o;
+        }
+    }
+    __syncthreads();
+    // V: element d, the step's 32 keys (4 blocks of 8 slots)
+#pragma unroll
+    for (int dd = 0; dd < VD; ++dd) {
+        const int d = tid + 256 * dd;
+        const int g = d / 64;
+        uint16_t* tile = as_global(P.band) + ((int64_t)bh * (P.nk / kStep + kBandPad) + step) * tile_elems<D>();
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            uint16_t* dst = tile + 8 * v_chunk_pos<D>(d, blk);
+            float x[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int k2 = 8 * blk + t, pos = p0 + k2;
+                const uint32_t c = VB == 8 ? (vw[dd][blk][t >> 2] >> (8 * (t & 3))) & 0xFFu : (vw[dd][blk][0] >> (4 * t)) & 0xFu;
+                const uint32_t sbw = vsb[k2][g];
+                x[t] = pos >= vis_lo && pos < len
+                           ? __builtin_fmaf((float)c, bf16_lo_to_f32(sbw), bf16_hi_to_f32(sbw)) : 0.0f;
+            }
+            const u32x4 o = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3]),
+                             bf16x2_rne(x[4], x[5]), bf16x2_rne(x[6], x[7])};
+            *reinterpret_cast<u32x4*>(dst) = o;
+        }
     }
 }
 
-// Register sets of in-flight step loads (NSET - 1 steps ahead of their use).
-template <int D, int KB, int VB>
-constexpr int pf_nset() { return D == 512 ? 3 : 4; }
+// ---------------------------------------------------------------------------
+// Attention over the dequantized band.
+//
+// A workgroup of 4 waves covers 64 query rows.  Each wave owns RT row tiles of
+// 16 rows; the 4 / (64 / (16 RT)) = NG wave groups take alternate steps (a key
+// split inside the workgroup) and merge in LDS at the end.
+template <int D> constexpr int pf_rt() { return D == 256 ? 2 : 1; }     // row tiles per wave
+template <int D> constexpr int pf_groups() { return pf_rt<D>(); }       // 4 waves x 16 RT rows = 64
 
-template <int D, int KB, int VB>
+template <int D>
+struct __attribute__((aligned(16))) PfSmem {
+    static constexpr int NG = pf_groups<D>();
+    uint16_t tile[2][NG][tile_elems<D>()];     // [buffer][key group]: step tiles
+};
+
+// Copy of one round's step tiles (NG consecutive band tiles, contiguous in the
+// workspace) into LDS buffer `slot` with LDS DMA: instruction j moves chunks
+// j*256 + tid (16 bytes per lane; a wave's 64 chunks are contiguous in LDS and
+// in the band), addressed as the round's base (scalar) plus the lane offset
+// tid*16 + j*4096 (a loop-invariant vector).  Inline assembly keeps the
+// compiler from ordering every later LDS read behind the copy: the caller waits
+// with vmcnt before the barrier that publishes the buffer.  Each statement
+// restores M0 (the LDS base of a DMA), which the compiler reserves.
+template <int D>
+__device__ __forceinline__ void dma_round(PfSmem<D>& sm, int slot, const uint16_t* src, int tid)
+{
+    constexpr int NJ = pf_groups<D>() * tile_elems<D>() / 8 / 256;   // instructions per thread
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&sm.tile[slot][0][0]) + (tid & ~63) * 16);
+    const uint64_t base = (uint64_t)(uintptr_t)src;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %1\n\t"
+                     "s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %2, %3\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "s"(lds0 + j * 4096), "v"((uint32_t)tid * 16u + j * 4096u), "s"(base)
+                     : "memory");
+    }
+}
+
+template <int D>
 __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<D>& sm)
 {
-    constexpr int NSET = pf_nset<D, KB, VB>();
-    constexpr int G = D / 64, DT = D / 16, KS = D / 32;
-    constexpr int KW = D * KB / 32;      // K words per slot
-    constexpr int VW = VB / 4;           // V words per (block, d)
-    using Codes = PfCodes<D, KB, VB>;
+    constexpr int NG = pf_groups<D>(), RT = pf_rt<D>();
+    constexpr int DT = D / 16, KS = D / 32;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, lg = lane >> 4;
+    const int grp = wave / (4 / NG);                      // key group: steps h with h % NG == grp
+    const int wrt = (wave % (4 / NG)) * RT;               // first row tile of this wave in the block
 
     // ---- work item: (b, kv head, 64-row block, split)
     const int S = P.S;
@@ -88,8 +236,9 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     const int rb = (idx / S) % n_rb;
     const int bh = idx / (S * n_rb);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
-    const int len = min(max(P.len[b], 0), P.max_len);
+    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
     const int R = P.R, W = P.W, C = P.C, hpk = P.hpk;
+    const int base0 = band_lo(len, C, W, R) & ~(kStep - 1);
 
     const int row0 = rb * kPfRows;
     const int last_row = min(row0 + kPfRows, P.n_rows) - 1;
@@ -103,201 +252,118 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
     const int st0 = j0 & ~(kStep - 1);
 
-    // ---- this wave's 16 rows and this lane's row
-    const int rt = rb * kPfWaves + wave;                  // 16-row tile index
-    const int wrow0 = rt * kRowTile;
+    // ---- this wave's row tiles and this lane's row in each
+    const int wrow0 = (rb * kPfWaves + wrt) * kRowTile;   // first row of the wave
     const bool wave_on = wrow0 < P.n_rows;
-    const int wlast = min(wrow0 + kRowTile, P.n_rows) - 1;
-    const int grow = wrow0 + m;
-    const bool row_ok = grow < P.n_rows;
-    const int qi = (row_ok ? grow : wrow0) / hpk;
-    const int hq = hkv * hpk + (row_ok ? grow : wrow0) % hpk;
-    const int p_row = len - C + qi;
-    int klo = max(j0, W > 0 ? p_row - W + 1 : 0);
-    int khi = min(j1 - 1, p_row);
-    if (!row_ok) { klo = 1; khi = 0; }
+    const int wlast = min(wrow0 + RT * kRowTile, P.n_rows) - 1;
+    int qi[RT], hq[RT], klo[RT], khi[RT];
+    bool row_ok[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int grow = wrow0 + r * kRowTile + m;
+        row_ok[r] = grow < P.n_rows;
+        qi[r] = (row_ok[r] ? grow : wrow0) / hpk;
+        hq[r] = hkv * hpk + (row_ok[r] ? grow : wrow0) % hpk;
+        const int p_row = len - C + qi[r];
+        klo[r] = max(j0, W > 0 ? p_row - W + 1 : 0);
+        khi[r] = min(j1 - 1, p_row);
+        if (!row_ok[r]) { klo[r] = 1; khi[r] = 0; }
+    }
     // keys every row of this wave sees
     const int full_lo = max(j0, W > 0 ? len - C + (wave_on ? wlast : wrow0) / hpk - W + 1 : 0);
     const int full_hi = min(j1 - 1, len - C + wrow0 / hpk);
 
-    const int64_t kslot0 = (int64_t)bh * R;
-    const uint32_t* __restrict__ kcodes = P.k_codes + kslot0 * KW;
-    const uint32_t* __restrict__ vcodes = P.v_codes + (int64_t)bh * (R / 8) * D * VW;
-
-    // ---- loads of one step into registers
-    const int k_key = tid >> 3, k_chunk = tid & 7;        // K dequant assignment
-    auto load_codes = [&](Codes& c, int st) {
-        const int st_mod = st % R;
-        const uint32_t* krow = kcodes + wrap_slot(st_mod + k_key, R) * KW + k_chunk * Codes::KWT;
-#pragma unroll
-        for (int w = 0; w < Codes::KWT; w += 4) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(krow + w);
-            c.k[w] = x.x; c.k[w + 1] = x.y; c.k[w + 2] = x.z; c.k[w + 3] = x.w;
-        }
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int vblk = wrap_slot(st_mod + 8 * blk, R) >> 3;
-#pragma unroll
-            for (int dd = 0; dd < Codes::VD; ++dd) {
-                const uint32_t* vw = vcodes + ((int64_t)vblk * D + tid + 256 * dd) * VW;
-                if constexpr (VB == 8) {
-                    const u32x2 x = *reinterpret_cast<const u32x2*>(vw);
-                    c.v[(dd * 4 + blk) * 2] = x.x;
-                    c.v[(dd * 4 + blk) * 2 + 1] = x.y;
-                } else {
-                    c.v[dd * 4 + blk] = vw[0];
-                }
-            }
-        }
-    };
-    // scale|bias words: thread t stages K word t and V word t of the step (32*G each)
-    constexpr int NSB = kStep * G;
-    const int sb_key = tid % kStep, sb_g = tid / kStep;
-    auto load_sb = [&](uint32_t (&w)[2], int st) {
-        const int o = NSB >= 256 || tid < NSB ? (int)(wrap_slot(st % R + sb_key, R) * G + (sb_g % G)) : 0;
-        w[0] = P.k_sb[kslot0 * G + o];
-        w[1] = P.v_sb[kslot0 * G + o];
-    };
-    auto stage_sb = [&](const uint32_t (&w)[2], int slot) {
-        if (NSB >= 256 || tid < NSB) {
-            const int g = sb_g % G, key = sb_key;
-            // V scale/bias go to the V^T element position of the key
-            const int j = key & 7;
-            const int pos = (key & ~7) + (VB == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1));
-            sm.ks[slot][g][key] = f16_bits(bf16_lo_to_f32(w[0]));
-            sm.kb[slot][g][key] = f16_bits(bf16_hi_to_f32(w[0]));
-            sm.vs[slot][g][pos] = f16_bits(bf16_lo_to_f32(w[1]));
-            sm.vb[slot][g][pos] = f16_bits(bf16_hi_to_f32(w[1]));
-        }
-    };
-    // ---- dequantize one step into LDS buffer `slot`
-    auto dequant = [&](const Codes& c, int slot) {
-        {   // K: 8 values per code word (4-bit) / 4 (8-bit), one group per thread
-            const int g = (k_chunk * (D / 8)) / 64;
-            const uint32_t sw = sm.ks[slot][g][k_key], bw = sm.kb[slot][g][k_key];
-            const f16x2 s2 = __builtin_bit_cast(f16x2, sw | (sw << 16));
-            const f16x2 b2 = __builtin_bit_cast(f16x2, bw | (bw << 16));
-            const int krow = 16 * ((k_key >> 2) & 1) + 4 * (k_key >> 3) + (k_key & 3);
-            _Float16* dst = &sm.kh[slot][krow][k_chunk * (D / 8)];
-#pragma unroll
-            for (int w = 0; w < Codes::KWT; w += (KB == 8 ? 2 : 1)) {
-                f16x2 pr[4];
-                if constexpr (KB == 8) {
-                    pr[0] = u8pair_to_f16x2(c.k[w], 0x04010400u);
-                    pr[1] = u8pair_to_f16x2(c.k[w], 0x04030402u);
-                    pr[2] = u8pair_to_f16x2(c.k[w + 1], 0x04010400u);
-                    pr[3] = u8pair_to_f16x2(c.k[w + 1], 0x04030402u);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pr[i] = u4pair_to_f16x2(c.k[w], i);
-                }
-                u32x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(pr[i], s2, b2));
-                *reinterpret_cast<u32x4*>(dst + (KB == 8 ? w * 4 : w * 8)) = o;
-            }
-        }
-#pragma unroll
-        for (int dd = 0; dd < Codes::VD; ++dd) {   // V: this thread's column d, 32 keys
-            const int d = tid + 256 * dd;
-            const int g = d / 64;
-            _Float16* dst = &sm.vt[slot][d][0];
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                f16x2 pr[4];
-                if constexpr (VB == 8) {
-                    const uint32_t w0 = c.v[(dd * 4 + blk) * 2], w1 = c.v[(dd * 4 + blk) * 2 + 1];
-                    pr[0] = u8pair_to_f16x2(w0, 0x04010400u);
-                    pr[1] = u8pair_to_f16x2(w0, 0x04030402u);
-                    pr[2] = u8pair_to_f16x2(w1, 0x04010400u);
-                    pr[3] = u8pair_to_f16x2(w1, 0x04030402u);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) pr[i] = u4pair_to_f16x2(c.v[dd * 4 + blk], i);
-                }
-                const u32x4 s4 = *reinterpret_cast<const u32x4*>(&sm.vs[slot][g][8 * blk]);
-                const u32x4 b4 = *reinterpret_cast<const u32x4*>(&sm.vb[slot][g][8 * blk]);
-                u32x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // element to a scalar first: bit_cast of a vector element expression
-                    // reads element 0 in this compiler
-                    const uint32_t sw = s4[i], bw = b4[i];
-                    o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
-                        pr[i], __builtin_bit_cast(f16x2, sw), __builtin_bit_cast(f16x2, bw)));
-                }
-                *reinterpret_cast<u32x4*>(dst + 8 * blk) = o;
-            }
-        }
+    // ---- step tiles of the band: round u copies band tiles t0 + NG*u .. +NG-1
+    const uint16_t* band_bh = as_global(P.band) + (int64_t)bh * (P.nk / kStep + kBandPad) * tile_elems<D>();
+    const int t0 = (st0 - base0) / kStep;
+    auto copy_round = [&](int u, int slot) {
+        dma_round<D>(sm, slot, band_bh + (int64_t)(t0 + NG * u) * tile_elems<D>(), tid);
     };
 
-    // ---- q of this lane's row as MFMA B operands, in the K element order
-    f16x8 qf[KS];
-    {
-        const uint16_t* qrow = P.q[0] + ((((int64_t)b * P.Hq + hq) * C + qi) * D);
+    // ---- q of this lane's rows as MFMA B operands (bf16, natural element order);
+    //      a lane past the last row reads the wave's first row and zeroes it
+    bf16x8 qf[RT][KS];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const uint16_t* qrow = as_global(P.q[0]) + ((((int64_t)b * P.Hq + hq[r]) * C + qi[r]) * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 u = 0;
-            if (row_ok) u = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { f[2 * e] = bf16_lo_to_f32(u[e]); f[2 * e + 1] = bf16_hi_to_f32(u[e]); }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)f[KB == 8 ? e : nib_order(e)];
+            u32x4 u = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+            if (!row_ok[r]) u = (u32x4)0;
+            qf[r][ks] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
     const float sl2e = P.scale_log2e;
-    f32x4 O[DT];
+    f32x4 O[RT][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[r][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run[RT], l_run[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }
 
-    // ---- one step of this wave's rows from LDS buffer `slot`
+    // ---- one step of this wave's rows from its group's LDS buffer `slot`
     auto compute = [&](int st, int slot, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        float z[8];
+        float z[RT][8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            f32x4 sacc = (f32x4){0.f, 0.f, 0.f, 0.f};
+            f32x4 sacc[RT];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) sacc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.kh[slot][16 * t + m][32 * ks + 8 * lg]);
-                sacc = mfma_f16(a, qf[ks], sacc);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &sm.tile[slot][grp][8 * k_chunk_pos<D>(16 * t + m, 4 * ks + lg)]);
+#pragma unroll
+                for (int r = 0; r < RT; ++r) sacc[r] = mfma_bf16(a, qf[r][ks], sacc[r]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (FULL) {
-                    z[4 * t + i] = sacc[i] * sl2e;
-                } else {
-                    const int key = st + 8 * lg + 4 * t + i;
-                    z[4 * t + i] = (key >= klo && key <= khi) ? sacc[i] * sl2e : -INFINITY;
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (FULL) {
+                        z[r][4 * t + i] = sacc[r][i] * sl2e;
+                    } else {
+                        const int key = st + 8 * lg + 4 * t + i;
+                        z[r][4 * t + i] = (key >= klo[r] && key <= khi[r]) ? sacc[r][i] * sl2e : -INFINITY;
+                    }
                 }
+        }
+        bf16x8 pb[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            float mloc = z[r][0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, z[r][k]);
+            const float mt = max_across_groups(mloc);
+            if (__any(mt > m_run[r] + kPfRescaleSlack)) {
+                const float m_new = fmaxf(m_run[r], mt);
+                const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) O[r][dt] *= alpha;
+                l_run[r] *= alpha;
+                m_run[r] = m_new;
             }
+            const float m_use = m_run[r] == -INFINITY ? 0.0f : m_run[r];
+            float p[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                p[k] = __builtin_amdgcn_exp2f(z[r][k] - m_use);
+                l_run[r] += p[k];
+            }
+            // p[k] is key 8*lg + k, the same order as the V^T columns
+            const u32x4 pw = {bf16x2_rne(p[0], p[1]), bf16x2_rne(p[2], p[3]),
+                              bf16x2_rne(p[4], p[5]), bf16x2_rne(p[6], p[7])};
+            pb[r] = __builtin_bit_cast(bf16x8, pw);
         }
-        float mloc = z[0];
-#pragma unroll
-        for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, z[k]);
-        const float mt = max_across_groups(mloc);
-        if (__any(mt > m_run + kPfRescaleSlack)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
-            l_run *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        float p[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { p[k] = __builtin_amdgcn_exp2f(z[k] - m_use); l_run += p[k]; }
-        f16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (_Float16)p[VB == 8 ? e : nib_order(e)];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.vt[slot][16 * dt + m][8 * lg]);
-            O[dt] = mfma_f16(a, pb, O[dt]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.tile[slot][grp][8 * v_chunk_pos<D>(16 * dt + m, lg)]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) O[r][dt] = mfma_bf16(a, pb[r], O[r][dt]);
         }
     };
     auto do_compute = [&](int st, int slot) {
@@ -306,95 +372,131 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
         else compute(st, slot, std::false_type{});
     };
 
-    // ---- pipeline over steps h = 0 .. nsteps-1, one barrier per step.  At step h:
-    //      issue the codes of step h+NSET and the scale|bias words of step
-    //      h+NSET+1, stage the scale|bias of step h+2 into LDS, dequantize step
-    //      h+1 and run the MFMAs of step h.  Every register set is consumed
-    //      NSET-1 steps after its loads were issued, so NSET-1 steps of loads
-    //      are in flight; loads are unconditional with the step index clamped.
-    //      Register sets rotate with h % NSET (compile-time indices), LDS
-    //      buffers with h & 1.
-    const int last = max(nsteps - 1, 0);
-    auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
-    Codes cs[NSET];
-    uint32_t sbs[NSET][2];
-    if (nsteps > 0) {
-        uint32_t s0[2];
-        load_sb(s0, stp(0));
-        static_for<0, NSET>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            load_codes(cs[r], stp(r));
-            load_sb(sbs[(r + 1) % NSET], stp(r + 1));
-        });
-        stage_sb(s0, 0);
-        stage_sb(sbs[1], 1);
-        __syncthreads();
-        dequant(cs[0], 0);
+    // ---- pipeline over rounds u = 0 .. nu-1; round u is step NG*u + g for key
+    //      group g (a step past nsteps computes nothing).  At round u: start the
+    //      copy of round u+1 into LDS buffer (u+1) & 1, run the MFMAs of round u
+    //      from buffer u & 1, wait for this thread's copies, one barrier.
+    const int nu = (nsteps + NG - 1) / NG;
+    copy_round(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int u = 0; u < nu; ++u) {
+        copy_round(u + 1, (u + 1) & 1);
+        const int h = NG * u + grp;
+        if (h < nsteps) do_compute(st0 + h * kStep, u & 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
-    for (int h0 = 0; h0 < nsteps; h0 += NSET) {
-        static_for<0, NSET>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const int h = h0 + r;
-            if (h >= nsteps) return;
-            const int slot = h & 1;
-            load_codes(cs[r], stp(h + NSET));
-            load_sb(sbs[(r + 1) % NSET], stp(h + NSET + 1));
-            stage_sb(sbs[(r + 2) % NSET], slot);
-            if (h + 1 < nsteps) dequant(cs[(r + 1) % NSET], slot ^ 1);
-            do_compute(st0 + h * kStep, slot);
-            __syncthreads();
-        });
+
+    // ---- merge the key groups: group g > 0 leaves (m, l, O) in LDS (the tile
+    //      buffers are free after the last barrier), group 0 folds them in
+    const int wig = wave % (4 / NG);                      // wave index within its group
+    if constexpr (NG > 1) {
+        static_assert(NG == 2, "two key groups");
+        float* xo = reinterpret_cast<float*>(&sm.tile[0][0][0]);        // [wig][r][dt][4][lane]
+        float* xm = xo + (4 / NG) * RT * DT * 4 * 64;                  // [wig][r][2][lane]
+        static_assert(sizeof(float) * ((4 / NG) * RT * (DT * 4 + 2) * 64) <= sizeof(PfSmem<D>), "merge fits");
+        if (grp == 1) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xo[(((wig * RT + r) * DT + dt) * 4 + i) * 64 + lane] = O[r][dt][i];
+                xm[((wig * RT + r) * 2 + 0) * 64 + lane] = m_run[r];
+                xm[((wig * RT + r) * 2 + 1) * 64 + lane] = l_run[r];
+            }
+        }
+        __syncthreads();
+        if (grp != 0) return;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float m1 = xm[((wig * RT + r) * 2 + 0) * 64 + lane];
+            const float l1 = xm[((wig * RT + r) * 2 + 1) * 64 + lane];
+            const float mm = fmaxf(m_run[r], m1);
+            const float a0 = m_run[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - mm);
+            const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    O[r][dt][i] = O[r][dt][i] * a0 + xo[(((wig * RT + r) * DT + dt) * 4 + i) * 64 + lane] * a1;
+            l_run[r] = l_run[r] * a0 + l1 * a1;
+            m_run[r] = mm;
+        }
     }
 
     // ---- write this wave's rows
-    if (!wave_on || !row_ok) return;
-    const float L = sum_across_groups(l_run);
+    if (!wave_on) return;
     const int dcol = 4 * lg;
-    if (S == 1) {
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        uint16_t* orow = P.out[0] + ((((int64_t)b * P.Hq + hq) * C + qi) * D);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const f32x4 o = O[dt] * inv;
-            uint2 w;
-            w.x = f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-            w.y = f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-            *reinterpret_cast<uint2*>(orow + dcol + 16 * dt) = w;
-        }
-    } else {
-        const int64_t ib = (int64_t)bh * P.n_rt + rt;
-        const int64_t prow = (ib * S + s) * kRowTile + m;
-        float* po = P.part + prow * D;
+    for (int r = 0; r < RT; ++r) {
+        const float L = sum_across_groups(l_run[r]);
+        if (!row_ok[r]) continue;
+        if (S == 1) {
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            uint16_t* orow = as_global(P.out[0]) + ((((int64_t)b * P.Hq + hq[r]) * C + qi[r]) * D);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
-        if (lg == 0) {
-            float* pml = P.part + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
-            pml[0] = m_run;
-            pml[1] = L;
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = O[r][dt] * inv;
+                uint2 w;
+                w.x = bf16x2_rne(o[0], o[1]);
+                w.y = bf16x2_rne(o[2], o[3]);
+                *reinterpret_cast<uint2*>(orow + dcol + 16 * dt) = w;
+            }
+        } else {
+            const int rt = rb * kPfWaves + wrt + r;       // 16-row tile index
+            const int64_t ib = (int64_t)bh * P.n_rt + rt;
+            const int64_t prow = (ib * S + s) * kRowTile + m;
+            float* po = as_global(P.part) + prow * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[r][dt];
+            if (lg == 0) {
+                float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
+                pml[0] = m_run[r];
+                pml[1] = L;
+            }
         }
     }
 }
 
-template <int D, int KB, int VB>
+// Workgroup i runs on XCD i % 8 (round-robin dispatch).  Consecutive work items
+// (the row blocks of one sequence and KV head, which all read the same band)
+// are given to one XCD, so the band is fetched into that XCD's L2 once and the
+// other row blocks hit it there.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int bid, int n)
+{
+    const int x = bid % kXcds, k = bid / kXcds;
+    const int q = n / kXcds, r = n % kXcds;
+    return x * q + min(x, r) + k;
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void prefill_kernel(AttnParams P)
 {
     __shared__ PfSmem<D> sm;
-    prefill_body<D, KB, VB>(P.d[0], blockIdx.x, sm);
+    prefill_body<D>(P.d[0], xcd_item(blockIdx.x, gridDim.x), sm);
 }
 
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream)
 {
-    const dim3 grid(total_items), block(256);
-    switch (p.d[0].cfg) {
-#define KVQ_PF(D_, KB_, VB_) \
+    const AttnDesc& d = p.d[0];
+    const dim3 dq_grid(d.nk / kStep, d.Hkv, d.B), block(256);
+    switch (d.cfg) {
+#define KVQ_DQ(D_, KB_, VB_) \
     case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
-        prefill_kernel<D_, KB_, VB_><<<grid, block, 0, stream>>>(p); break;
-    KVQ_PF(256, 4, 4) KVQ_PF(256, 4, 8) KVQ_PF(256, 8, 4) KVQ_PF(256, 8, 8)
-    KVQ_PF(512, 4, 4) KVQ_PF(512, 4, 8) KVQ_PF(512, 8, 4) KVQ_PF(512, 8, 8)
-#undef KVQ_PF
+        band_dequant_kernel<D_, KB_, VB_><<<dq_grid, block, 0, stream>>>(d); break;
+    KVQ_DQ(256, 4, 4) KVQ_DQ(256, 4, 8) KVQ_DQ(256, 8, 4) KVQ_DQ(256, 8, 8)
+    KVQ_DQ(512, 4, 4) KVQ_DQ(512, 4, 8) KVQ_DQ(512, 8, 4) KVQ_DQ(512, 8, 8)
+#undef KVQ_DQ
     default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d.D == 256) prefill_kernel<256><<<dim3(total_items), block, 0, stream>>>(p);
+    else if (d.D == 512) prefill_kernel<512><<<dim3(total_items), block, 0, stream>>>(p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
