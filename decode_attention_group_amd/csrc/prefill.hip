@@ -17,8 +17,8 @@
 //     rows (in MFMA row order) and then its D V^T rows (keys contiguous per
 //     element), 16-byte chunks XOR-swizzled so the MFMA operand reads hit
 //     distinct banks.  Band positions outside what the chunk can see are zeros.
-//   prefill_kernel: one workgroup of 4 waves per (sequence, KV head, 64 query
-//     rows, split).  Tiles are copied global -> LDS with LDS DMA (no register
+//   prefill_kernel: one workgroup per (sequence, KV head, 64 query rows,
+//     split).  Tiles are copied global -> LDS with LDS DMA (no register
 //     staging) one round ahead of their use.  Each wave owns RT row tiles of
 //     16 rows, so every K / V^T operand read from LDS feeds RT MFMAs (LDS
 //     bandwidth bounds the one-tile-per-wave layout); the NG wave groups take
@@ -177,11 +177,15 @@ __global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
 // ---------------------------------------------------------------------------
 // Attention over the dequantized band.
 //
-// A workgroup of 4 waves covers 64 query rows.  Each wave owns RT row tiles of
-// 16 rows; the 4 / (64 / (16 RT)) = NG wave groups take alternate steps (a key
-// split inside the workgroup) and merge in LDS at the end.
-template <int D> constexpr int pf_rt() { return D == 256 ? 2 : 1; }     // row tiles per wave
-template <int D> constexpr int pf_groups() { return pf_rt<D>(); }       // 4 waves x 16 RT rows = 64
+// A workgroup covers 64 query rows.  Each wave owns RT row tiles of 16 rows, so
+// 4 / RT waves cover the block; NG such wave groups take alternate steps (a key
+// split inside the workgroup) and merge in LDS at the end.  head_dim 256 runs
+// 8 waves (two per SIMD, so one wave's softmax overlaps another's MFMAs and LDS
+// reads); head_dim 512 needs all 512 registers of a lane for its 32 output
+// tiles and runs 4.
+template <int D> constexpr int pf_rt() { return 1; }                    // row tiles per wave
+template <int D> constexpr int pf_groups() { return D == 256 ? 2 : 1; } // key groups
+template <int D> constexpr int pf_waves() { return kPfWaves / pf_rt<D>() * pf_groups<D>(); }
 
 template <int D>
 struct __attribute__((aligned(16))) PfSmem {
@@ -190,17 +194,19 @@ struct __attribute__((aligned(16))) PfSmem {
 };
 
 // Copy of one round's step tiles (NG consecutive band tiles, contiguous in the
-// workspace) into LDS buffer `slot` with LDS DMA: instruction j moves chunks
-// j*256 + tid (16 bytes per lane; a wave's 64 chunks are contiguous in LDS and
-// in the band), addressed as the round's base (scalar) plus the lane offset
-// tid*16 + j*4096 (a loop-invariant vector).  Inline assembly keeps the
+// workspace) into LDS buffer `slot` with LDS DMA: with NT threads, instruction j
+// moves chunks j*NT + tid (16 bytes per lane; a wave's 64 chunks are contiguous
+// in LDS and in the band), addressed as the round's base (scalar) plus the lane
+// offset 16*(tid + j*NT) (a loop-invariant vector).  Inline assembly keeps the
 // compiler from ordering every later LDS read behind the copy: the caller waits
 // with vmcnt before the barrier that publishes the buffer.  Each statement
 // restores M0 (the LDS base of a DMA), which the compiler reserves.
 template <int D>
 __device__ __forceinline__ void dma_round(PfSmem<D>& sm, int slot, const uint16_t* src, int tid)
 {
-    constexpr int NJ = pf_groups<D>() * tile_elems<D>() / 8 / 256;   // instructions per thread
+    constexpr int NT = 64 * pf_waves<D>();                           // threads
+    constexpr int NJ = pf_groups<D>() * tile_elems<D>() / 8 / NT;    // instructions per thread
+    static_assert(NJ * NT * 8 == pf_groups<D>() * tile_elems<D>(), "whole chunks per thread");
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&sm.tile[slot][0][0]) + (tid & ~63) * 16);
     const uint64_t base = (uint64_t)(uintptr_t)src;
 #pragma unroll
@@ -212,7 +218,7 @@ __device__ __forceinline__ void dma_round(PfSmem<D>& sm, int slot, const uint16_
                      "global_load_lds_dwordx4 %2, %3\n\t"
                      "s_mov_b32 m0, %0"
                      : "=&s"(saved)
-                     : "s"(lds0 + j * 4096), "v"((uint32_t)tid * 16u + j * 4096u), "s"(base)
+                     : "s"(lds0 + j * NT * 16), "v"((uint32_t)tid * 16u + j * NT * 16u), "s"(base)
                      : "memory");
     }
 }
@@ -221,13 +227,14 @@ template <int D>
 __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<D>& sm)
 {
     constexpr int NG = pf_groups<D>(), RT = pf_rt<D>();
+    constexpr int RW = kPfWaves / RT;                     // waves per key group
     constexpr int DT = D / 16, KS = D / 32;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, lg = lane >> 4;
-    const int grp = wave / (4 / NG);                      // key group: steps h with h % NG == grp
-    const int wrt = (wave % (4 / NG)) * RT;               // first row tile of this wave in the block
+    const int grp = wave / RW;                            // key group: steps h with h % NG == grp
+    const int wrt = (wave % RW) * RT;                     // first row tile of this wave in the block
 
     // ---- work item: (b, kv head, 64-row block, split)
     const int S = P.S;
@@ -390,12 +397,12 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
 
     // ---- merge the key groups: group g > 0 leaves (m, l, O) in LDS (the tile
     //      buffers are free after the last barrier), group 0 folds them in
-    const int wig = wave % (4 / NG);                      // wave index within its group
+    const int wig = wave % RW;                            // wave index within its group
     if constexpr (NG > 1) {
         static_assert(NG == 2, "two key groups");
         float* xo = reinterpret_cast<float*>(&sm.tile[0][0][0]);        // [wig][r][dt][4][lane]
-        float* xm = xo + (4 / NG) * RT * DT * 4 * 64;                  // [wig][r][2][lane]
-        static_assert(sizeof(float) * ((4 / NG) * RT * (DT * 4 + 2) * 64) <= sizeof(PfSmem<D>), "merge fits");
+        float* xm = xo + RW * RT * DT * 4 * 64;                        // [wig][r][2][lane]
+        static_assert(sizeof(float) * (RW * RT * (DT * 4 + 2) * 64) <= sizeof(PfSmem<D>), "merge fits");
         if (grp == 1) {
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
@@ -473,7 +480,7 @@ __device__ __forceinline__ int xcd_item(int bid, int n)
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnParams P)
+__global__ __launch_bounds__(64 * pf_waves<D>()) void prefill_kernel(AttnParams P)
 {
     __shared__ PfSmem<D> sm;
     prefill_body<D>(P.d[0], xcd_item(blockIdx.x, gridDim.x), sm);
@@ -494,8 +501,8 @@ hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stre
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.D == 256) prefill_kernel<256><<<dim3(total_items), block, 0, stream>>>(p);
-    else if (d.D == 512) prefill_kernel<512><<<dim3(total_items), block, 0, stream>>>(p);
+    if (d.D == 256) prefill_kernel<256><<<dim3(total_items), dim3(64 * pf_waves<256>()), 0, stream>>>(p);
+    else if (d.D == 512) prefill_kernel<512><<<dim3(total_items), dim3(64 * pf_waves<512>()), 0, stream>>>(p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
