@@ -84,50 +84,55 @@ __global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
     constexpr int VW = VB / 4;               // V code words per (block, d)
     constexpr int KE = D / 8;                // K elements per thread
     __shared__ uint32_t vsb[kStep][G];       // V scale|bias words of the step
+    static_assert(kStep * G <= 256, "one V scale|bias word per thread");
     const int tid = threadIdx.x;
     const int step = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
     const int bh = b * P.Hkv + hkv;
-    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
     const int R = P.R;
-    const int vis_lo = band_lo(len, P.C, P.W, R);
-    const int base0 = vis_lo & ~(kStep - 1);
-    const int p0 = base0 + step * kStep;
-    if (p0 >= len) return;                   // past every query: never read
     const int64_t kslot0 = (int64_t)bh * R;
-
-    // Every load is issued before any store (stores in between would order
-    // the loads behind them): the V scale|bias words to LDS, then the K codes
-    // and scale|bias word and the V codes to registers.
-    for (int i = tid; i < kStep * G; i += 256) {
-        const int key = i / G, g = i % G;
-        vsb[key][g] = as_global(P.v_sb)[(kslot0 + (p0 + key) % R) * G + g];
-    }
     const int key = tid >> 3, ch = tid & 7;              // K: key tid/8, elements [KE*(tid%8), +KE)
-    const int kpos = p0 + key;
-    const bool kok = kpos >= vis_lo && kpos < len;
-    const int64_t kslot = kslot0 + kpos % R;
     constexpr int KWT = KE * KB / 32;                     // K code words per thread
-    uint32_t kw[KWT];
-    {
+    constexpr int VD = (D + 255) / 256;                   // elements d per thread
+
+    // len[b] (a vector load, waited for only where it is used) arrives while
+    // the codes are requested for len = max_len, the common case; another len
+    // requests them again.  Every load is issued before any store (stores in
+    // between would order the loads behind them).
+    int oz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(oz));
+    const int len_lane = as_global(P.len)[b + oz];
+    int len, vis_lo, p0;
+    uint32_t vsbw, kw[KWT], ksbw, vw[VD][4][VW];
+    auto issue = [&](int l) {
+        len = l;
+        vis_lo = band_lo(len, P.C, P.W, R);
+        p0 = (vis_lo & ~(kStep - 1)) + step * kStep;
+        vsbw = tid < kStep * G ? as_global(P.v_sb)[(kslot0 + (p0 + tid / G) % R) * G + tid % G] : 0u;
+        const int64_t kslot = kslot0 + (p0 + key) % R;
         const uint32_t* src = as_global(P.k_codes) + kslot * KW + ch * KWT;
 #pragma unroll
         for (int w = 0; w < KWT; w += 4) {
             const u32x4 x = *reinterpret_cast<const u32x4*>(src + w);
             kw[w] = x.x; kw[w + 1] = x.y; kw[w + 2] = x.z; kw[w + 3] = x.w;
         }
-    }
-    const uint32_t ksbw = as_global(P.k_sb)[kslot * G + ch * KE / 64];
-    constexpr int VD = (D + 255) / 256;                   // elements d per thread
-    uint32_t vw[VD][4][VW];
+        ksbw = as_global(P.k_sb)[kslot * G + ch * KE / 64];
 #pragma unroll
-    for (int dd = 0; dd < VD; ++dd)
+        for (int dd = 0; dd < VD; ++dd)
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int slot8 = (p0 + 8 * blk) % R;            // a multiple of 8
-            const uint32_t* src = as_global(P.v_codes) + (((int64_t)bh * (R / 8) + slot8 / 8) * D + tid + 256 * dd) * VW;
+            for (int blk = 0; blk < 4; ++blk) {
+                const int slot8 = (p0 + 8 * blk) % R;            // a multiple of 8
+                const uint32_t* vsrc = as_global(P.v_codes) + (((int64_t)bh * (R / 8) + slot8 / 8) * D + tid + 256 * dd) * VW;
 #pragma unroll
-            for (int w = 0; w < VW; ++w) vw[dd][blk][w] = src[w];
-        }
+                for (int w = 0; w < VW; ++w) vw[dd][blk][w] = vsrc[w];
+            }
+    };
+    issue(P.max_len);
+    const int len_act = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
+    if (len_act != len) issue(len_act);
+    if (p0 >= len) return;                   // past every query: never read
+    if (tid < kStep * G) vsb[tid / G][tid % G] = vsbw;
+    const int kpos = p0 + key;
+    const bool kok = kpos >= vis_lo && kpos < len;
 
     {   // K
         const float sc = bf16_lo_to_f32(ksbw), bi = bf16_hi_to_f32(ksbw);
@@ -243,27 +248,22 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     const int rb = (idx / S) % n_rb;
     const int bh = idx / (S * n_rb);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
-    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
     const int R = P.R, W = P.W, C = P.C, hpk = P.hpk;
-    const int base0 = band_lo(len, C, W, R) & ~(kStep - 1);
+    // len[b] (a vector load, waited for only where it is used) arrives while
+    // the q rows and the first band tiles are requested for len = max_len,
+    // the common case; another len re-plans and copies again.
+    int oz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(oz));
+    const int len_lane = as_global(P.len)[b + oz];
 
+    // ---- this wave's row tiles and this lane's row in each
     const int row0 = rb * kPfRows;
     const int last_row = min(row0 + kPfRows, P.n_rows) - 1;
     const int qi_lo = row0 / hpk, qi_hi = last_row / hpk;
-    int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
-    lo = max(lo, max(0, len - R));
-    const int hi = len - C + qi_hi;
-    const int base = lo & ~(kStep - 1);
-    const int j0 = max(lo, base + s * P.split_len);
-    const int j1 = min(hi + 1, base + (s + 1) * P.split_len);
-    const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
-    const int st0 = j0 & ~(kStep - 1);
-
-    // ---- this wave's row tiles and this lane's row in each
     const int wrow0 = (rb * kPfWaves + wrt) * kRowTile;   // first row of the wave
     const bool wave_on = wrow0 < P.n_rows;
     const int wlast = min(wrow0 + RT * kRowTile, P.n_rows) - 1;
-    int qi[RT], hq[RT], klo[RT], khi[RT];
+    int qi[RT], hq[RT];
     bool row_ok[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -271,21 +271,7 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
         row_ok[r] = grow < P.n_rows;
         qi[r] = (row_ok[r] ? grow : wrow0) / hpk;
         hq[r] = hkv * hpk + (row_ok[r] ? grow : wrow0) % hpk;
-        const int p_row = len - C + qi[r];
-        klo[r] = max(j0, W > 0 ? p_row - W + 1 : 0);
-        khi[r] = min(j1 - 1, p_row);
-        if (!row_ok[r]) { klo[r] = 1; khi[r] = 0; }
     }
-    // keys every row of this wave sees
-    const int full_lo = max(j0, W > 0 ? len - C + (wave_on ? wlast : wrow0) / hpk - W + 1 : 0);
-    const int full_hi = min(j1 - 1, len - C + wrow0 / hpk);
-
-    // ---- step tiles of the band: round u copies band tiles t0 + NG*u .. +NG-1
-    const uint16_t* band_bh = as_global(P.band) + (int64_t)bh * (P.nk / kStep + kBandPad) * tile_elems<D>();
-    const int t0 = (st0 - base0) / kStep;
-    auto copy_round = [&](int u, int slot) {
-        dma_round<D>(sm, slot, band_bh + (int64_t)(t0 + NG * u) * tile_elems<D>(), tid);
-    };
 
     // ---- q of this lane's rows as MFMA B operands (bf16, natural element order);
     //      a lane past the last row reads the wave's first row and zeroes it
@@ -298,6 +284,49 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
             u32x4 u = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
             if (!row_ok[r]) u = (u32x4)0;
             qf[r][ks] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+
+    // ---- key ranges for a given len: the block's keys [j0, j1) in nsteps steps
+    //      from st0, each row's [klo, khi], the keys every row of the wave sees
+    //      [full_lo, full_hi], and the band tile t0 of step st0
+    int j0, j1, nsteps, st0, full_lo, full_hi, t0;
+    int klo[RT], khi[RT];
+    auto plan = [&](int len) {
+        const int base0 = band_lo(len, C, W, R) & ~(kStep - 1);
+        int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
+        lo = max(lo, max(0, len - R));
+        const int hi = len - C + qi_hi;
+        const int base = lo & ~(kStep - 1);
+        j0 = max(lo, base + s * P.split_len);
+        j1 = min(hi + 1, base + (s + 1) * P.split_len);
+        nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
+        st0 = j0 & ~(kStep - 1);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int p_row = len - C + qi[r];
+            klo[r] = max(j0, W > 0 ? p_row - W + 1 : 0);
+            khi[r] = min(j1 - 1, p_row);
+            if (!row_ok[r]) { klo[r] = 1; khi[r] = 0; }
+        }
+        full_lo = max(j0, W > 0 ? len - C + (wave_on ? wlast : wrow0) / hpk - W + 1 : 0);
+        full_hi = min(j1 - 1, len - C + wrow0 / hpk);
+        t0 = (st0 - base0) / kStep;
+    };
+
+    // ---- step tiles of the band: round u copies band tiles t0 + NG*u .. +NG-1
+    const uint16_t* band_bh = as_global(P.band) + (int64_t)bh * (P.nk / kStep + kBandPad) * tile_elems<D>();
+    auto copy_round = [&](int u, int slot) {
+        dma_round<D>(sm, slot, band_bh + (int64_t)(t0 + NG * u) * tile_elems<D>(), tid);
+    };
+    plan(P.max_len);
+    copy_round(0, 0);
+    {
+        const int len = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
+        if (len != P.max_len) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the first copy lands before the second
+            plan(len);
+            copy_round(0, 0);
         }
     }
 
@@ -384,7 +413,6 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     //      copy of round u+1 into LDS buffer (u+1) & 1, run the MFMAs of round u
     //      from buffer u & 1, wait for this thread's copies, one barrier.
     const int nu = (nsteps + NG - 1) / NG;
-    copy_round(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int u = 0; u < nu; ++u) {
