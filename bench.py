@@ -166,6 +166,12 @@ class Runner:
             spec = wl.caches[0]
             g = self.caches["kv"][0]
             nbytes = kvq.kvq_decode_workspace_bytes([(g, self.q["kv"], self.out["kv"], self.len["kv"], spec.length, 1.0)])
+            nbytes = max(nbytes, kvq.kvq_decode_step_workspace_bytes(g, wl.queries[0].Hq, spec.length))
+            k, v = self.step_kv["kv"]
+            self.step_k1 = k.reshape(spec.B, spec.Hkv, spec.D)
+            self.step_v1 = v.reshape(spec.B, spec.Hkv, spec.D)
+        # decode steps run as one fused call (append + read); the others as two
+        self.fused = wl.kind == "decode"
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
@@ -185,13 +191,24 @@ class Runner:
             kvq.kvq_attn_decode(self.caches["kv"][r], self.q["kv"][0], self.len["kv"], wl.caches[0].length,
                                 1.0, out=self.out["kv"][0], workspace=self.ws)
 
-    def _graph(self, steps, first, with_append):
+    def step(self, r):
+        """One decode step as the fused call: the token's append and the read."""
+        self.kvq.kvq_decode_step(self.caches["kv"][r], self.step_k1, self.step_v1, self.q["kv"][0],
+                                 self.len["kv"], self.wl.caches[0].length, 1.0, out=self.out["kv"][0],
+                                 workspace=self.ws)
+
+    def _graph(self, steps, first, mode):
+        """mode: "step" (fused where the workload has it), "two" (append, then
+        read), "attn" (the read alone)."""
         torch = self.torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
                 r = (first + i) % self.nrep
-                if with_append:
+                if mode == "step" and self.fused:
+                    self.step(r)
+                    continue
+                if mode != "attn":
                     self.append(r)
                 self.attend(r)
         return g
@@ -204,9 +221,12 @@ class Runner:
         for i in range(warmup):
             self.append(i % self.nrep)
             self.attend(i % self.nrep)
+            if self.fused:
+                self.step(i % self.nrep)
         torch.cuda.synchronize()
-        g_step = self._graph(steps, warmup, True)
-        g_attn = self._graph(steps, warmup, False)
+        g_step = self._graph(steps, warmup, "step")
+        g_two = self._graph(steps, warmup, "two") if self.fused else None
+        g_attn = self._graph(steps, warmup, "attn")
         # Evict the last-level cache by reading 1 GiB: a read leaves clean lines,
         # whereas a write fill would leave dirty ones whose write-back would be
         # charged to the first timed steps.
@@ -225,7 +245,8 @@ class Runner:
 
         step_ms = float(np.median([timed(g_step, k) for k in range(reps)]))
         attn_ms = float(np.median([timed(g_attn, k) for k in range(reps)]))
-        del flush, g_step, g_attn
+        self.two_call_ms = float(np.median([timed(g_two, k) for k in range(reps)])) if g_two else None
+        del flush, g_step, g_attn, g_two
         return step_ms, attn_ms
 
 
@@ -274,7 +295,8 @@ def measure(name, steps, warmup, rotate_gib, with_cpu):
     step_ms, attn_ms = runner.run(steps, warmup)
     byts, flops = algorithmic(wl)
     res = {"workload": name, "ms_per_step": step_ms, "attn_ms": attn_ms, "bytes": byts, "flops": flops,
-           "replicas": runner.nrep}
+           "replicas": runner.nrep, "fused_step": runner.fused,
+           "two_call_ms_per_step": None if runner.two_call_ms is None else round(runner.two_call_ms, 5)}
     if wl.kind == "prefill":
         res.update(value=flops / (step_ms * 1e-3) / 1e12, unit="TFLOP/s",
                    roofline={"bound": "mfma", "achieved": round(flops / (attn_ms * 1e-3) / 1e12, 3),
@@ -331,7 +353,8 @@ def main():
             if name == args.workload:
                 continue
             r = measure(name, args.steps, args.warmup, args.rotate_gib, False)
-            others[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "attn_ms", "replicas")}
+            others[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "attn_ms", "replicas",
+                                              "two_call_ms_per_step")}
             others[name]["roofline_frac"] = r["roofline"]["frac"]
             others[name]["achieved"] = r["roofline"]["achieved"]
             print(f"# {name}: {r['value']:.2f} {r['unit']} step {r['ms_per_step'] * 1e3:.1f} us, "
@@ -355,11 +378,13 @@ def main():
         "config": {"workload": args.workload, "batch": spec.B, "head_dim": spec.D, "q_heads": wl.queries[0].Hq,
                    "kv_heads": spec.Hkv, "k_bits": spec.k_bits, "v_bits": spec.v_bits, "window": spec.window,
                    "cached_tokens": spec.length, "replicas": head["replicas"],
-                   "step": "append the step's token(s) + attention read",
+                   "step": ("kvq_decode_step: the token's append and the attention read in one call"
+                            if head["fused_step"] else "append the step's token(s) + attention read"),
                    "compute": "4/8-bit codes -> fp16 MFMA, fp32 accumulate, bf16 out"},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
         "attn_ms": round(head["attn_ms"], 5),
+        "two_call_ms_per_step": head["two_call_ms_per_step"],
         "configs": others,
     }
     print(json.dumps(line), flush=True)

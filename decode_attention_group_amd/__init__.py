@@ -33,8 +33,9 @@ MAX_SHARED_GROUPS = 4
 SIZE_MAX = (1 << 64) - 1
 
 # Symbols include/kvq.h declares.
-EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_attn_prefill_chunk", "kvq_attn_decode_shared",
-           "kvq_decode_workspace_bytes", "kvq_prefill_workspace_bytes", "kvq_last_error")
+EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+           "kvq_attn_decode_shared", "kvq_decode_workspace_bytes", "kvq_decode_step_workspace_bytes",
+           "kvq_prefill_workspace_bytes", "kvq_last_error")
 
 
 class KvqUnavailable(RuntimeError):
@@ -80,6 +81,9 @@ def load_library(path: str = LIB_PATH):
     GP = ctypes.POINTER(SharedGroupStruct)
     lib.kvq_append_quantize.argtypes = [CP, P, P, i32, P, P]
     lib.kvq_attn_decode.argtypes = [CP, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
+    lib.kvq_decode_step.argtypes = [CP, P, P, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
+    lib.kvq_decode_step_workspace_bytes.argtypes = [CP, i32, i32]
+    lib.kvq_decode_step_workspace_bytes.restype = sz
     lib.kvq_attn_prefill_chunk.argtypes = [CP, P, i32, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_attn_decode_shared.argtypes = [GP, i32, P, sz, P]
     lib.kvq_decode_workspace_bytes.argtypes = [GP, i32]
@@ -88,7 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_prefill_workspace_bytes.restype = sz
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
-    for name in ("kvq_append_quantize", "kvq_attn_decode", "kvq_attn_prefill_chunk", "kvq_attn_decode_shared"):
+    for name in ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+                 "kvq_attn_decode_shared"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -213,6 +218,36 @@ def kvq_attn_decode(cache: KVCache, q: torch.Tensor, len_: torch.Tensor, max_len
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.kvq_attn_decode(ctypes.byref(cache.struct), _ptr(q), q.shape[1], _ptr(len_), int(max_len),
                                float(scale), _ptr(out), _ptr(ws), wsb, _stream()))
+    return out
+
+
+def kvq_decode_step_workspace_bytes(cache: KVCache, n_q_heads: int, max_len: int) -> int:
+    n = load_library().kvq_decode_step_workspace_bytes(ctypes.byref(cache.struct), n_q_heads, max_len)
+    if n == SIZE_MAX:
+        raise KvqError(1, "invalid arguments for kvq_decode_step_workspace_bytes")
+    return n
+
+
+def kvq_decode_step(cache: KVCache, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, len_: torch.Tensor,
+                    max_len: int, scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Append k, v fp32 [B][H][D] at position len-1 and read: q bf16 [B][Hq][D] -> out bf16 [B][Hq][D]."""
+    lib = load_library()
+    _gpu(k, "k", torch.float32)
+    _gpu(v, "v", torch.float32)
+    _gpu(q, "q", torch.bfloat16)
+    _gpu(len_, "len", torch.int32)
+    B, H, D = k.shape
+    if tuple(v.shape) != tuple(k.shape) or (B, H, D) != (cache.batch, cache.n_kv_heads, cache.head_dim):
+        raise ValueError("k/v shape does not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _gpu(out, "out", torch.bfloat16)
+    nbytes = kvq_decode_step_workspace_bytes(cache, q.shape[1], max_len)
+    ws = _workspace(nbytes, workspace, q.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.kvq_decode_step(ctypes.byref(cache.struct), _ptr(k), _ptr(v), _ptr(q), q.shape[1], _ptr(len_),
+                               int(max_len), float(scale), _ptr(out), _ptr(ws), wsb, _stream()))
     return out
 
 

@@ -6,34 +6,14 @@
 // One workgroup owns one 8-slot block of one (sequence, KV head) cache, for K
 // or for V, so the blocked V words of that block are read-merged-written by a
 // single workgroup: no two workgroups of a call touch the same word.
-// Eight consecutive lanes quantize one 64-value group (8 values each); the
-// group's min and max meet through three butterfly shuffles.
+// Eight consecutive lanes quantize one 64-value group (8 values each).
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "quant.h"
 
 namespace kvq {
 
 #pragma clang fp contract(off)
-
-// Largest bf16 value <= x (x finite): clearing the low 16 bits moves toward
-// zero, which is downward only for x >= 0; a negative x steps one bf16 unit
-// further from zero instead.
-__device__ __forceinline__ float bf16_round_down(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0xFFFFu) == 0u) return x;
-    const uint32_t t = u & 0xFFFF0000u;
-    return __uint_as_float((u & 0x80000000u) ? t + 0x10000u : t);
-}
-
-// Smallest bf16 value >= x (x finite, here always >= 0).
-__device__ __forceinline__ float bf16_round_up(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0xFFFFu) == 0u) return x;
-    const uint32_t t = u & 0xFFFF0000u;
-    return __uint_as_float((u & 0x80000000u) ? t : t + 0x10000u);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
@@ -78,46 +58,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
         const float4 a = *reinterpret_cast<const float4*>(src);
         const float4 c = *reinterpret_cast<const float4*>(src + 4);
         float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        float mn = v[0], mx = v[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, o));
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-        }
-        mn = mn + 0.0f;                       // -0 reads as +0
-        mx = mx + 0.0f;
-        const float bias = bf16_round_down(mn);
-        const float step = (mx - bias) / (float)top;
-        const float scale = bf16_round_up(step);
         uint32_t q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float r = 0.0f;
-            if (scale != 0.0f) {
-                r = __builtin_rintf((v[e] - bias) / scale);
-                r = fminf(fmaxf(r, 0.0f), (float)top);
-            }
-            q[e] = (uint32_t)r;
-        }
+        float scale, bias;
+        quantize_group8(v, top, q, scale, bias);
         const int slot = blk * 8 + j;
         if ((ch & 7) == 0)
-            sb[(bh * R + slot) * G + (ch >> 3)] =
-                (__float_as_uint(scale) >> 16) | (__float_as_uint(bias) & 0xFFFF0000u);
+            sb[(bh * R + slot) * G + (ch >> 3)] = sb_word(scale, bias);
         if (!is_v) {
-            uint32_t* row = codes + (bh * R + slot) * (int64_t)(D * bits / 32);
-            if (bits == 8) {
-                uint2 w;
-                w.x = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-                w.y = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-                *reinterpret_cast<uint2*>(row + ch * 2) = w;
-            } else {
-                uint32_t w = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w |= q[e] << (4 * e);
-                row[ch] = w;
-            }
+            store_k_chunk(codes + (bh * R + slot) * (int64_t)(D * bits / 32), ch, bits, q);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vcode[j][ch * 8 + e] = (uint8_t)q[e];

@@ -27,6 +27,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "quant.h"
 
 namespace kvq {
 
@@ -105,7 +106,104 @@ struct VRegs {
 // rescaling: probabilities are taken against a stale max and may reach 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
+// Fused decode step.  The token at position len-1 is quantized here with the
+// append kernel's device code (so the codes are the same bit for bit), written
+// into the cache by the item of row tile 0, and attended from its dequantized
+// values as one more split of every item: for each row, m = scale*log2(e) *
+// (q . khat), l = 1, o = vhat; the other splits leave that position out.  The
+// V words of the token's 8-slot block are read, merged and written while other
+// workgroups may be reading them: only the token's own bits change, so either
+// order gives them the other slots' codes.
 template <int D, int KB, int VB>
+__device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float* lds)
+{
+    constexpr int NT = 64 * Shape<D>::NW;           // threads
+    constexpr int G = D / 64, CH = D / 8, VW = VB / 4;
+    constexpr int PARTS = NT / kRowTile;            // lanes per query row in the dot product
+    constexpr int EPP = D / PARTS;                  // elements per lane
+    static_assert(2 * CH <= NT && EPP % 8 == 0, "one chunk per thread");
+    static_assert((2 * D * 4 + D) <= (int)sizeof(AttnSmem<D>), "fits the attention LDS");
+    float* khat = lds;
+    float* vhat = lds + D;
+    uint8_t* vq = reinterpret_cast<uint8_t*>(lds + 2 * D);
+    const int tid = threadIdx.x;
+    const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
+    const int R = P.R;
+    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 1), P.max_len);
+    const int slot = (len - 1) % R;
+    const bool writer = rt == 0;
+    // the cache arrays of a fused step are the caller's writable cache
+    uint32_t* k_codes = const_cast<uint32_t*>(as_global(P.k_codes));
+    uint32_t* v_codes = const_cast<uint32_t*>(as_global(P.v_codes));
+    uint32_t* k_sb = const_cast<uint32_t*>(as_global(P.k_sb));
+    uint32_t* v_sb = const_cast<uint32_t*>(as_global(P.v_sb));
+    if (tid < 2 * CH) {                              // lanes [0, CH): K chunks; [CH, 2CH): V chunks
+        const bool is_v = tid >= CH;
+        const int ch = is_v ? tid - CH : tid;
+        const float* src = as_global(is_v ? P.v_new : P.k_new) + ((int64_t)bh * D + ch * 8);
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 c = *reinterpret_cast<const float4*>(src + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        uint32_t q[8];
+        float scale, bias;
+        quantize_group8(v, is_v ? (1 << VB) - 1 : (1 << KB) - 1, q, scale, bias);
+        float* xh = is_v ? vhat : khat;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xh[ch * 8 + e] = (float)q[e] * scale + bias;
+        if (writer) {
+            if ((ch & 7) == 0) (is_v ? v_sb : k_sb)[((int64_t)bh * R + slot) * G + ch / 8] = sb_word(scale, bias);
+            if (!is_v) store_k_chunk(k_codes + ((int64_t)bh * R + slot) * (D * KB / 32), ch, KB, q);
+            else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vq[ch * 8 + e] = (uint8_t)q[e];
+            }
+        }
+    }
+    __syncthreads();
+    if (writer) {                                    // the token's bits of its V block
+        const int t = slot & 7;
+        for (int d = tid; d < D; d += NT) {
+            uint32_t* w = v_codes + (((int64_t)bh * (R / 8) + slot / 8) * D + d) * VW;
+            if constexpr (VB == 4) {
+                w[0] = (w[0] & ~(0xFu << (4 * t))) | ((uint32_t)vq[d] << (4 * t));
+            } else {
+                const int wi = t >> 2, sh = 8 * (t & 3);
+                w[wi] = (w[wi] & ~(0xFFu << sh)) | ((uint32_t)vq[d] << sh);
+            }
+        }
+    }
+    // q . khat for each row of the tile: PARTS consecutive lanes per row
+    const int r = tid / PARTS, part = tid % PARTS;
+    const int grow = rt * kRowTile + r;
+    const bool row_ok = grow < P.n_rows;
+    const RowMap rm = map_row(P, hkv, row_ok ? grow : rt * kRowTile);
+    const uint16_t* qrow = as_global(P.q[0]) + ((((int64_t)b * P.Hq + rm.hq) * P.C + rm.qi) * D + part * EPP);
+    const float* kh = khat + part * EPP;
+    float acc = 0.0f;
+#pragma unroll
+    for (int e0 = 0; e0 < EPP; e0 += 8) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(qrow + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc += bf16_lo_to_f32(u[i]) * kh[e0 + 2 * i] + bf16_hi_to_f32(u[i]) * kh[e0 + 2 * i + 1];
+    }
+#pragma unroll
+    for (int o = 1; o < PARTS; o <<= 1) acc += __shfl_xor(acc, o);
+    if (!row_ok) return;
+    const int64_t prow = (((int64_t)bh * P.n_rt + rt) * P.S + s) * kRowTile + r;
+    float* po = as_global(P.part) + prow * D + part * EPP;
+#pragma unroll
+    for (int e0 = 0; e0 < EPP; e0 += 4)
+        *reinterpret_cast<f32x4*>(po + e0) = *reinterpret_cast<const f32x4*>(vhat + part * EPP + e0);
+    if (part == 0) {
+        float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * P.S * kRowTile * D + prow * 2;
+        pml[0] = acc * P.scale_log2e;
+        pml[1] = 1.0f;
+    }
+}
+
+// STEP: the descriptor may be a fused decode step (single-descriptor launches only).
+template <int D, int KB, int VB, bool STEP = false>
 __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D>& sm)
 {
     using Sh = Shape<D>;
@@ -124,6 +222,10 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const int rt = (idx / S) % P.n_rt;
     const int bh = idx / (S * P.n_rt);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
+    if (STEP && P.k_new != nullptr && s == S - 1) {
+        new_token_split<D, KB, VB>(P, bh, rt, s, (float*)(__attribute__((address_space(3))) float*)(&sm));
+        return;
+    }
     const int R = P.R, W = P.W, C = P.C;
     // len[b] is read in flight: the ranges below are first taken for the
     // common case len == max_len, so the first code loads go out without
@@ -147,16 +249,16 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     auto ranges = [&](int len) {
         int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
         lo = max(lo, max(0, len - R));
-        const int hi = len - C + qi_hi;
+        const int hi = len - C + qi_hi - P.excl;
         const int base = lo & ~(kStep - 1);
         j0 = max(lo, base + s * P.split_len);
         j1 = min(hi + 1, base + (s + 1) * P.split_len);
         // keys every row of the tile sees (steps inside need no mask)
         full_lo = max(j0, W > 0 ? len - C + qi_hi - W + 1 : 0);
-        full_hi = min(j1 - 1, len - C + qi_lo);
+        full_hi = min(j1 - 1, len - C + qi_lo - P.excl);
         const int p_row = len - C + rm.qi;
         klo = max(j0, W > 0 ? p_row - W + 1 : 0);
-        khi = min(j1 - 1, p_row);
+        khi = min(j1 - 1, p_row - P.excl);
         if (!row_ok) { klo = 1; khi = 0; }
     };
     ranges(P.max_len);
@@ -534,7 +636,7 @@ __global__ __launch_bounds__(64 * Shape<D>::NW) void attn_kernel(AttnParams P)
     __shared__ AttnSmem<D> sm;
     const int bid = blockIdx.x;
     if constexpr (ONE) {
-        attn_body<D, KB, VB>(P.d[0], bid, sm);
+        attn_body<D, KB, VB, true>(P.d[0], bid, sm);
     } else {
         const int di = find_desc(P, bid);
         attn_body<D, KB, VB>(P.d[di], bid - P.d[di].item_begin, sm);
@@ -566,7 +668,7 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
     }
 }
 
-// One workgroup per (descriptor, row tile item, row, 64-column chunk):
+// One workgroup per (descriptor, sequence and KV head, row, 64-column chunk):
 // out = sum_s w_s o_s / sum_s w_s l_s, w_s = 2^(m_s - max m).  The 256 threads
 // are 16 column quads x 16 split lanes.  Each split lane issues the loads of all
 // its splits first, then folds them with a running max, so the partials are
@@ -591,13 +693,11 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
     int ir = bid - d.comb_begin;
     const int ch = ir % nch;
     ir /= nch;
-    const int r = ir % kRowTile;
-    const int ib = ir / kRowTile;
-    const int rt = ib % d.n_rt;
-    const int bh = ib / d.n_rt;
+    const int grow = ir % d.n_rows;          // row of the (sequence, KV head)
+    const int bh = ir / d.n_rows;
     const int b = bh / d.Hkv, hkv = bh - b * d.Hkv;
-    const int grow = rt * kRowTile + r;
-    if (grow >= d.n_rows) return;
+    const int r = grow % kRowTile;
+    const int ib = bh * d.n_rt + grow / kRowTile;
     const float* po = as_global(d.part);
     const float* pml = as_global(d.part) + (size_t)d.B * d.Hkv * d.n_rt * S * kRowTile * D;
     const int tid = threadIdx.x;
@@ -690,7 +790,7 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t stream)
     int blocks = 0;
     for (int i = 0; i < p.n_desc; ++i)
         if (p.d[i].S > 1)
-            blocks = p.d[i].comb_begin + p.d[i].B * p.d[i].Hkv * p.d[i].n_rt * kRowTile * (p.d[i].D / kCombCols);
+            blocks = p.d[i].comb_begin + p.d[i].B * p.d[i].Hkv * p.d[i].n_rows * (p.d[i].D / kCombCols);
     if (blocks == 0) return hipSuccess;
     combine_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(p);
     return hipGetLastError();

@@ -79,6 +79,8 @@ struct ReadSpec {
     const int32_t* len;
     int max_len;
     int C;             // 1: decode rows are layers x heads; > 1: prefill rows are queries x heads
+    const float* k_new = nullptr;   // fused decode step: the step's K and V rows, appended by the read
+    const float* v_new = nullptr;
 };
 
 kvq_status check_read(const ReadSpec& r, const char* what)
@@ -153,10 +155,18 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
     const int forced = env_splits();
     if (forced > 0) S = forced;
-    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
+    // a fused step adds one split per item for the new token
+    const int64_t max_s = r.k_new ? kvq::kMaxSplits - 1 : kvq::kMaxSplits;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, max_s)));
     const int64_t steps_per = (steps + S - 1) / S;
     d.split_len = (int)(steps_per * kvq::kStep);
     d.S = (int)((steps + steps_per - 1) / steps_per);
+    if (r.k_new) {
+        d.k_new = r.k_new;
+        d.v_new = r.v_new;
+        d.excl = 1;
+        d.S += 1;
+    }
     d.n_items = (int)(items * d.S);
 }
 
@@ -184,7 +194,7 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         d.item_begin = total_items;
         total_items += d.n_items;
         d.comb_begin = comb;
-        if (d.S > 1) comb += d.B * d.Hkv * d.n_rt * kvq::kRowTile * (d.D / 64);
+        if (d.S > 1) comb += d.B * d.Hkv * d.n_rows * (d.D / 64);
         const size_t f = kvq::part_floats(d);
         ws = (ws + 255) & ~(size_t)255;
         if (f) ws += f * sizeof(float);
@@ -376,6 +386,35 @@ KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, in
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
+    return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+}
+
+KVQ_API size_t kvq_decode_step_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_len)
+{
+    if (check_cache(cache, "kvq_decode_step_workspace_bytes") != KVQ_OK) return SIZE_MAX;
+    if (n_q_heads < 1 || n_q_heads % cache->n_kv_heads != 0 || max_len < 1) return SIZE_MAX;
+    static const float dummy = 0.0f;
+    ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, 1, &dummy, &dummy};
+    kvq::AttnParams P;
+    int total = 0;
+    return plan_all(&r, 1, P, total);
+}
+
+KVQ_API kvq_status kvq_decode_step(const kvq_cache* cache, const float* k, const float* v,
+                                   const uint16_t* q, int32_t n_q_heads,
+                                   const int32_t* len, int32_t max_len, float scale,
+                                   uint16_t* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    const char* what = "kvq_decode_step";
+    const uint16_t* qs[1] = {q};
+    uint16_t* os[1] = {out};
+    ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1, k, v};
+    kvq_status st = check_read(r, what);
+    if (st != KVQ_OK) return st;
+    if (!k || !v) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k or v is NULL", what);
+    if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k and v must be 16-byte aligned", what);
     return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
 }
 

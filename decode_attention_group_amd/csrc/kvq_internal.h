@@ -39,6 +39,9 @@ struct AttnDesc {
     const uint16_t* q[KVQ_MAX_SHARED_LAYERS];
     uint16_t* out[KVQ_MAX_SHARED_LAYERS];
     const int32_t* len;
+    const float* k_new;     // fused decode step: the step's fp32 K and V rows [B][Hkv][D]
+    const float* v_new;     //   (null otherwise); split S-1 of every item takes that token
+    int32_t excl;           // 1: the attention splits leave out position len-1 (fused step)
     float* part;            // split partials (null when S == 1)
     uint16_t* band;         // prefill: dequantized band tiles, bf16 [B][Hkv][nk/32][64*D] (the
                             // LDS image of each 32-key step: K rows, then V^T rows, swizzled)

@@ -143,6 +143,32 @@ kvq_status kvq_attn_decode(const kvq_cache *cache,
                            hipStream_t stream);
 
 /*
+ * One decode step of a layer: append this step's token of every sequence and
+ * read the cache with it (page 80, model.ts attentionTraining: appendWindow of
+ * the new keys and values, then read.attend(q, scale); decode declaration: one
+ * new token per sequence).  Equivalent to
+ *   kvq_append_quantize(cache, k, v, 1, pos0 = len - 1) followed by
+ *   kvq_attn_decode(cache, q, ..., len, ...),
+ * with the same codes written bit for bit, in one attention launch (plus the
+ * combine): the new token is quantized, written and attended from its
+ * dequantized values by one more split per KV head while the other splits read
+ * the older positions.
+ *   k, v   fp32 [B][H][D], 16-byte aligned: the step's key (after norm and RoPE)
+ *          and value of each sequence and KV head
+ *   len    int32 [B], tokens including this one; it goes to slot (len[b]-1) mod R
+ *   q, n_q_heads, max_len, scale, out  as for kvq_attn_decode
+ *   workspace  at least kvq_decode_step_workspace_bytes() bytes; needs no clearing
+ * k, v must be finite with |x| <= 1e38.
+ */
+kvq_status kvq_decode_step(const kvq_cache *cache,
+                           const float *k, const float *v,
+                           const uint16_t *q, int32_t n_q_heads,
+                           const int32_t *len, int32_t max_len, float scale,
+                           uint16_t *out,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * One chunked-prefill read (page 80, model.ts prompt / promptChunk: a whole chunk
  * of a prompt per sequence): the chunk's C tokens were appended first; query i of
  * sequence b sits at p = len[b] - C + i and sees max(0, p-W+1) .. p -- causal
@@ -190,6 +216,10 @@ kvq_status kvq_attn_decode_shared(const kvq_shared_group *groups, int32_t n_grou
  * kvq_attn_decode call pass one group with n_layers = 1.  Returns 0 when the
  * call needs none, and SIZE_MAX when the arguments are invalid. */
 size_t kvq_decode_workspace_bytes(const kvq_shared_group *groups, int32_t n_groups);
+
+/* (host) Workspace bytes for kvq_decode_step with these arguments (SIZE_MAX when
+ * they are invalid). */
+size_t kvq_decode_step_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads, int32_t max_len);
 
 /* (host) Workspace bytes for kvq_attn_prefill_chunk with these arguments. */
 size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads,
