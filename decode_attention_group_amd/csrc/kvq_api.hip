@@ -338,7 +338,7 @@ size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
         vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kPrefillRows + d.hpk - 1) / d.hpk);
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
-    const int kTargetWg = 128;     // one 256-thread workgroup on half the CUs before splitting keys
+    const int kTargetWg = 128;     // workgroups to reach before splitting keys (a split adds a combine)
     int64_t S = (kTargetWg + items - 1) / items;
     const int forced = env_splits();
     if (forced > 0) S = forced;

@@ -83,7 +83,7 @@ hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStre
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);
 
-// Query rows per prefill workgroup (4 waves x 16 rows).
-constexpr int kPrefillRows = 64;
+// Query rows per prefill workgroup (two 16-row tiles).
+constexpr int kPrefillRows = 32;
 
 }  // namespace kvq

@@ -17,7 +17,7 @@
 //     rows (in MFMA row order) and then its D V^T rows (keys contiguous per
 //     element), 16-byte chunks XOR-swizzled so the MFMA operand reads hit
 //     distinct banks.  Band positions outside what the chunk can see are zeros.
-//   prefill_kernel: one workgroup per (sequence, KV head, 64 query rows,
+//   prefill_kernel: one workgroup per (sequence, KV head, 32 query rows,
 //     split).  Tiles are copied global -> LDS with LDS DMA (no register
 //     staging) one round ahead of their use.  Each wave owns RT row tiles of
 //     16 rows, so every K / V^T operand read from LDS feeds RT MFMAs (LDS
@@ -34,7 +34,7 @@
 
 namespace kvq {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 2;                    // row tiles per workgroup
 constexpr int kPfRows = kPfWaves * kRowTile;   // query rows per workgroup
 constexpr float kPfRescaleSlack = 8.0f;
 // Band tiles kept per (sequence, KV head): the band's steps plus kBandPad more,
@@ -182,12 +182,12 @@ __global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
 // ---------------------------------------------------------------------------
 // Attention over the dequantized band.
 //
-// A workgroup covers 64 query rows.  Each wave owns RT row tiles of 16 rows, so
-// 4 / RT waves cover the block; NG such wave groups take alternate steps (a key
-// split inside the workgroup) and merge in LDS at the end.  head_dim 256 runs
-// 8 waves (two per SIMD, so one wave's softmax overlaps another's MFMAs and LDS
-// reads); head_dim 512 needs all 512 registers of a lane for its 32 output
-// tiles and runs 4.
+// A workgroup covers 32 query rows (two row tiles: the 8192 rows of a 512-query
+// chunk fill 256 workgroups, one per CU).  Each wave owns RT row tiles of 16
+// rows, so 2 / RT waves cover the block; NG such wave groups take alternate
+// steps (a key split inside the workgroup) and merge in LDS at the end.
+// head_dim 256 runs two key groups (4 waves); head_dim 512 one (its 32 output
+// tiles take most of a lane's registers and the step tiles twice the LDS).
 template <int D> constexpr int pf_rt() { return 1; }                    // row tiles per wave
 template <int D> constexpr int pf_groups() { return D == 256 ? 2 : 1; } // key groups
 template <int D> constexpr int pf_waves() { return kPfWaves / pf_rt<D>() * pf_groups<D>(); }
@@ -241,7 +241,7 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     const int grp = wave / RW;                            // key group: steps h with h % NG == grp
     const int wrt = (wave % RW) * RT;                     // first row tile of this wave in the block
 
-    // ---- work item: (b, kv head, 64-row block, split)
+    // ---- work item: (b, kv head, 32-row block, split)
     const int S = P.S;
     const int n_rb = (P.n_rt + kPfWaves - 1) / kPfWaves;
     const int s = idx % S;
