@@ -20,9 +20,9 @@
 //   (the second term for all groups at once in one fp16 MFMA per step).
 // Scales and biases of a step are staged in LDS.  The online-softmax max is
 // reduced across the four 16-lane groups of the wave with lane shuffles.
-// Each workgroup has 4 waves that take alternate steps of its key range and
-// merge (max, sum, output) through LDS at the end; a split with S > 1 leaves
-// fp32 partials that the combine kernel reduces.
+// The waves of a workgroup split head_dim (see Shape); their partial scores meet
+// in LDS once per step.  A split with S > 1 leaves fp32 partials (output, max,
+// sum) that the combine kernel reduces.
 #include <type_traits>
 
 #include "kvq_device.h"
