@@ -159,7 +159,7 @@ class Runner:
                             for qs in wl.queries] for r in range(self.nrep)]
             nbytes = kvq.kvq_decode_workspace_bytes(
                 [(g.cache, g.q, g.out, g.len, g.max_len, g.scale) for g in self.groups[0]])
-        elif wl.kind == "prefill":
+        elif wl.kind in ("prefill", "verify"):
             spec = wl.caches[0]
             nbytes = kvq.kvq_prefill_workspace_bytes(self.caches["kv"][0], wl.queries[0].Hq, self.C, spec.length)
         else:
@@ -184,7 +184,7 @@ class Runner:
         kvq, wl = self.kvq, self.wl
         if wl.kind == "shared":
             kvq.kvq_attn_decode_shared(self.groups[r], workspace=self.ws)
-        elif wl.kind == "prefill":
+        elif wl.kind in ("prefill", "verify"):
             kvq.kvq_attn_prefill_chunk(self.caches["kv"][r], self.q["kv"][0], self.len["kv"], wl.caches[0].length,
                                        1.0, out=self.out["kv"][0], workspace=self.ws)
         else:

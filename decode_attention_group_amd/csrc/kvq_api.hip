@@ -311,11 +311,19 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
     return plan_all(rs, n_groups, P, total);
 }
 
-// Prefill with head_dim 256 or 512 runs the band dequant + prefill kernels (the
-// chunk's key band dequantized once to bf16 in the workspace, then 64 query
-// rows per workgroup).  Other head_dims use the decode kernel with per-row
-// positions.
-bool use_prefill_kernel(const kvq_cache* c, int chunk) { return chunk > 1 && c->head_dim >= 256; }
+// Prefill with head_dim 256 or 512 and more than 64 query rows per KV head runs
+// the band dequant + prefill kernels (the chunk's key band dequantized once to
+// bf16 in the workspace, then 32 query rows per workgroup).  Shorter chunks
+// (speculative-verify windows: a few tokens per sequence) and head_dim 128 use
+// the decode kernel with per-row positions, which reads the codes directly: a
+// band would be dequantized for only a handful of rows.
+bool use_prefill_kernel(const kvq_cache* c, int n_q_heads, int chunk)
+{
+    const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "decode": force a path (measurement)
+    const bool can = chunk > 1 && c->head_dim >= 256;
+    if (e && *e) return can && e[0] == 'b';
+    return can && (int64_t)chunk * (n_q_heads / c->n_kv_heads) > 64;
+}
 
 // Band positions per (b, kv head): every position a query of the chunk can see,
 // from a step-aligned start.
@@ -373,7 +381,7 @@ KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_h
     ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, chunk};
     kvq::AttnParams P;
     int total = 0;
-    return use_prefill_kernel(cache, chunk) ? plan_prefill(r, P, total) : plan_all(&r, 1, P, total);
+    return use_prefill_kernel(cache, n_q_heads, chunk) ? plan_prefill(r, P, total) : plan_all(&r, 1, P, total);
 }
 
 KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
@@ -429,7 +437,7 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, chunk};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
-    if (!use_prefill_kernel(cache, chunk)) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+    if (!use_prefill_kernel(cache, n_q_heads, chunk)) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
     kvq::AttnParams P;
     int total_items = 0;
     const size_t need = plan_prefill(r, P, total_items);

@@ -52,7 +52,7 @@ class QuerySpec:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "decode" | "prefill" | "shared"
+    kind: str            # "decode" | "prefill" | "verify" (a few queries per sequence) | "shared"
     caches: Tuple[CacheSpec, ...]
     queries: Tuple[QuerySpec, ...]
     seed: int = 0
@@ -88,6 +88,16 @@ WORKLOADS: Dict[str, Workload] = {
             [QuerySpec("kv", 1, 8, 512)],
             "chunked prefill, B2, 512-query chunk after 8192 cached tokens, 8 q / 2 kv heads, "
             "D256, K4/V4, window 512 (ring of 1024)"),
+        _wl("verify_b8_c5_w512", "verify",
+            [CacheSpec("kv", 8, 2, 256, 4, 8, 520, 512, 4096)],
+            [QuerySpec("kv", 1, 8, 5)],
+            "speculative verify window, B8, 5 queries per sequence (4 drafted + 1), 8 q / 2 kv heads, "
+            "D256, K4/V8, window 512 (ring of 520)"),
+        _wl("verify_b4_c5_l32768", "verify",
+            [CacheSpec("kv", 4, 1, 512, 8, 8, 32768, 0, 32768)],
+            [QuerySpec("kv", 1, 8, 5)],
+            "speculative verify window on a full layer, B4, 5 queries per sequence, 8 q / 1 kv head, "
+            "D512, K8/V8, cached length 32768"),
         _wl("shared_decode_b32", "shared",
             [CacheSpec("donor", 32, 2, 256, 4, 4, 512, 512, 16384),
              CacheSpec("full", 32, 1, 512, 8, 8, 16384, 0, 16384)],

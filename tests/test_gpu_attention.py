@@ -209,16 +209,62 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "band", "decode"])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_prefill_small(case):
+def test_prefill_small(case, path):
+    """Every case on the path the library picks and on each path forced
+    (the band kernels exist for head_dim 256 and 512 only)."""
     B, Hq, Hkv, D, kb, vb, R, W, L, C = case
-    print(f"prefill {case}", flush=True)
+    print(f"prefill {case} path={path}", flush=True)
     g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case))
     q = small_q_bits(sum(case) + 1, (B, Hq, C, D), D ** -0.25)
     lens = np.full(B, L, np.int32)
+    if path != "auto":
+        os.environ["KVQ_PREFILL_PATH"] = path
+    try:
+        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("KVQ_PREFILL_PATH", None)
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill {case} path={path}")
+
+
+VERIFY_CASES = [
+    # B, Hq, Hkv, D, kb, vb, R, W, L, C: a few queries per sequence (draft tokens + 1)
+    (2, 8, 2, 256, 4, 8, 520, 512, 1500, 5),     # ring wrap, window 512
+    (1, 8, 1, 512, 8, 8, 2048, 0, 1000, 2),      # full layer, two rows per head: one tile
+    (3, 4, 4, 128, 8, 4, 256, 100, 700, 8),      # MHA, head_dim 128
+    (2, 16, 2, 256, 8, 4, 136, 128, 333, 8),     # 64 rows per KV head: four row tiles
+    (1, 8, 2, 512, 4, 4, 64, 60, 64, 5),         # window + chunk fill the ring exactly
+]
+
+
+@pytest.mark.parametrize("case", VERIFY_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_verify_window(case):
+    """Short causal chunks (speculative verify): ragged lengths, against the oracle."""
+    B, Hq, Hkv, D, kb, vb, R, W, L, C = case
+    print(f"verify {case}", flush=True)
+    g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case) + 3)
+    q = small_q_bits(sum(case) + 4, (B, Hq, C, D), D ** -0.25)
+    lens = np.array([L - (b % 2) * min(7, L - C) for b in range(B)], np.int32)
     out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
     torch.cuda.synchronize()
-    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill {case}")
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"verify {case}")
+
+
+@pytest.mark.parametrize("name", ["verify_b8_c5_w512", "verify_b4_c5_l32768"])
+def test_verify_workload(name):
+    wl = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
+    gpu, orc, qd, _ = build_workload(wl)
+    spec = wl.caches[0]
+    q = qd[0][0]
+    lens = np.full(spec.B, spec.length, np.int32)
+    out = kvq.kvq_attn_prefill_chunk(gpu["kv"], q_dev(q), torch.from_numpy(lens).cuda(), spec.length)
+    torch.cuda.synchronize()
+    o, _ = orc["kv"]
+    mx, mean = assert_close(torch_bf16_to_f64(out), o.attend(q, lens), name)
+    print(f"{name}: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("splits", ["1", "3", "7"])
