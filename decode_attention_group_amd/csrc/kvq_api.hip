@@ -311,18 +311,32 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
     return plan_all(rs, n_groups, P, total);
 }
 
-// Prefill with head_dim 256 or 512 and more than 64 query rows per KV head runs
-// the band dequant + prefill kernels (the chunk's key band dequantized once to
-// bf16 in the workspace, then 32 query rows per workgroup).  Shorter chunks
-// (speculative-verify windows: a few tokens per sequence) and head_dim 128 use
-// the decode kernel with per-row positions, which reads the codes directly: a
-// band would be dequantized for only a handful of rows.
-bool use_prefill_kernel(const kvq_cache* c, int n_q_heads, int chunk)
+// Kernel path of a chunk read:
+//   decode: head_dim 128, or a short chunk over a short key range: the decode
+//     kernel with per-row positions (each 16-row tile reads the keys; for a
+//     window of a few hundred keys the re-reads are cheaper than the
+//     alternatives: 15.6 us against 18.1 us for 5 queries x 8 heads of B8 over
+//     a 512-key window);
+//   codes:  head_dim 256/512, up to 64 rows per KV head over more than 2048
+//     keys (speculative-verify windows on full layers): each workgroup holds
+//     all the rows, so every key is read once, and dequantizes each step into
+//     LDS once (prefill_codes.hip; 88 us against 120 us on the decode path for
+//     5 queries x 8 heads of B4 over 32768 keys of head_dim 512);
+//   band:   longer chunks: the chunk's key band is dequantized once into the
+//     workspace as bf16, then 32 query rows per workgroup (prefill.hip).
+enum class ChunkPath { kDecode, kCodes, kBand };
+
+ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
 {
-    const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "decode": force a path (measurement)
-    const bool can = chunk > 1 && c->head_dim >= 256;
-    if (e && *e) return can && e[0] == 'b';
-    return can && (int64_t)chunk * (n_q_heads / c->n_kv_heads) > 64;
+    const bool big = chunk > 1 && c->head_dim >= 256;
+    const int64_t rows = (int64_t)chunk * (n_q_heads / c->n_kv_heads);
+    const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "codes" / "decode": force (measurement)
+    if (e && *e) return !big ? ChunkPath::kDecode : e[0] == 'b' ? ChunkPath::kBand
+                                                  : e[0] == 'c' ? ChunkPath::kCodes : ChunkPath::kDecode;
+    if (!big || rows <= kvq::kRowTile) return ChunkPath::kDecode;
+    if (rows > kvq::kCodesPrefillRows) return ChunkPath::kBand;
+    const int64_t keys = c->window > 0 ? std::min<int64_t>((int64_t)c->window + chunk - 1, max_len) : max_len;
+    return keys > 2048 ? ChunkPath::kCodes : ChunkPath::kDecode;
 }
 
 // Band positions per (b, kv head): every position a query of the chunk can see,
@@ -365,6 +379,35 @@ size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
     return part + (size_t)d.B * d.Hkv * (d.nk + 4 * kvq::kStep) * d.D * 2 * sizeof(uint16_t);
 }
 
+// Short-chunk kernel: one workgroup per (b, kv head, 64-row block, split); the
+// workspace holds the split partials only.
+size_t plan_codes(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
+{
+    std::memset(&P, 0, sizeof(P));
+    P.n_desc = 1;
+    plan_read(r, 1, P.d[0]);                      // shape fields
+    kvq::AttnDesc& d = P.d[0];
+    const kvq_cache* c = r.cache;
+    const int n_rb = (d.n_rows + kvq::kCodesPrefillRows - 1) / kvq::kCodesPrefillRows;
+    int64_t vis = r.max_len;
+    if (c->window > 0)
+        vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kCodesPrefillRows + d.hpk - 1) / d.hpk);
+    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
+    const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
+    // resident workgroups: two per CU for head_dim 256, one for 512 (its LDS)
+    const int kTargetWg = d.D == 512 ? 256 : 512;
+    int64_t S = (kTargetWg + items - 1) / items;
+    const int forced = env_splits();
+    if (forced > 0) S = forced;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
+    const int64_t steps_per = (steps + S - 1) / S;
+    d.split_len = (int)(steps_per * kvq::kStep);
+    d.S = (int)((steps + steps_per - 1) / steps_per);
+    d.n_items = (int)(items * d.S);
+    total_items = d.n_items;
+    return kvq::part_floats(d) * sizeof(float);
+}
+
 void bind_prefill_workspace(kvq::AttnParams& P, void* workspace)
 {
     kvq::AttnDesc& d = P.d[0];
@@ -381,7 +424,11 @@ KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_h
     ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, chunk};
     kvq::AttnParams P;
     int total = 0;
-    return use_prefill_kernel(cache, n_q_heads, chunk) ? plan_prefill(r, P, total) : plan_all(&r, 1, P, total);
+    switch (chunk_path(cache, n_q_heads, chunk, max_len)) {
+    case ChunkPath::kBand: return plan_prefill(r, P, total);
+    case ChunkPath::kCodes: return plan_codes(r, P, total);
+    default: return plan_all(&r, 1, P, total);
+    }
 }
 
 KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
@@ -437,12 +484,24 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, chunk};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
-    if (!use_prefill_kernel(cache, n_q_heads, chunk)) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+    const ChunkPath path = chunk_path(cache, n_q_heads, chunk, max_len);
+    if (path == ChunkPath::kDecode) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
     kvq::AttnParams P;
     int total_items = 0;
-    const size_t need = plan_prefill(r, P, total_items);
+    const size_t need = path == ChunkPath::kBand ? plan_prefill(r, P, total_items) : plan_codes(r, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
+    if (path == ChunkPath::kCodes) {
+        P.d[0].part = kvq::part_floats(P.d[0]) ? static_cast<float*>(workspace) : nullptr;
+        if (trace_on())
+            fprintf(stderr, "[kvq] %s short-chunk kernel: B=%d Hkv=%d Hq=%d D=%d C=%d rows=%d S=%d split=%d wg=%d\n",
+                    what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].C, P.d[0].n_rows, P.d[0].S,
+                    P.d[0].split_len, total_items);
+        hipError_t e = kvq::launch_prefill_codes(P, total_items, stream);
+        if (e == hipSuccess) e = kvq::launch_combine(P, stream);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+        return ok();
+    }
     bind_prefill_workspace(P, workspace);
     if (trace_on())
         fprintf(stderr, "[kvq] %s prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d split=%d wg=%d band=%d\n",

@@ -82,8 +82,12 @@ hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);
+hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_t stream);
 
 // Query rows per prefill workgroup (two 16-row tiles).
 constexpr int kPrefillRows = 32;
+// Query rows per workgroup of the short-chunk kernel (4 waves x 16 rows): a chunk
+// with at most this many rows per KV head reads each key once.
+constexpr int kCodesPrefillRows = 64;
 
 }  // namespace kvq

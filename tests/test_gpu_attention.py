@@ -209,11 +209,11 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["auto", "band", "decode"])
+@pytest.mark.parametrize("path", ["auto", "band", "codes", "decode"])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_prefill_small(case, path):
     """Every case on the path the library picks and on each path forced
-    (the band kernels exist for head_dim 256 and 512 only)."""
+    (the band and short-chunk kernels exist for head_dim 256 and 512 only)."""
     B, Hq, Hkv, D, kb, vb, R, W, L, C = case
     print(f"prefill {case} path={path}", flush=True)
     g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case))
@@ -236,6 +236,8 @@ VERIFY_CASES = [
     (3, 4, 4, 128, 8, 4, 256, 100, 700, 8),      # MHA, head_dim 128
     (2, 16, 2, 256, 8, 4, 136, 128, 333, 8),     # 64 rows per KV head: four row tiles
     (1, 8, 2, 512, 4, 4, 64, 60, 64, 5),         # window + chunk fill the ring exactly
+    (2, 8, 1, 512, 8, 8, 4096, 0, 3000, 5),      # full layer, > 2048 keys: the short-chunk kernel
+    (1, 16, 2, 256, 4, 8, 4096, 0, 2500, 4),     # the same at head_dim 256, 32 rows per KV head
 ]
 
 
