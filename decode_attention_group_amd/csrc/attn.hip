@@ -387,19 +387,20 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
             bf16x8 ab;
             {
+                // k-slot k = 8*lg + e < NSLOT holds term k/(3*GPW) (0: the bias, 1: the
+                // scale) of group k%GPW.  The group words are read unconditionally and
+                // picked with selects: an LDS read under a lane-dependent condition
+                // would become a branch with its own wait, once per slot.
+                uint32_t wg[GPW];
+#pragma unroll
+                for (int gi = 0; gi < GPW; ++gi) wg[gi] = sm.ksb[wave][gi][kk];
                 uint32_t hw[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int k = 8 * lg + e;
-                    uint32_t v = 0;
-#pragma unroll
-                    for (int q = 0; q < NSLOT; ++q)
-                        if (q == k) {
-                            const int term = q / (3 * GPW), gi = q % GPW;
-                            const uint32_t w = sm.ksb[wave][gi][kk];
-                            v = term == 0 ? (w >> 16) : (w & 0xFFFFu);
-                        }
-                    hw[e] = v;
+                    const uint32_t w = wg[GPW - 1] ^ ((k % GPW == 0) ? (wg[0] ^ wg[GPW - 1]) : 0u);
+                    const uint32_t v = k / (3 * GPW) == 0 ? (w >> 16) : (w & 0xFFFFu);
+                    hw[e] = k < NSLOT ? v : 0u;
                 }
                 const u32x4 w = {hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
                                  hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)};
@@ -484,11 +485,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
         {
             f16x8 pb, ac;
-            u32x4 w0 = 0, w1 = 0;
-            if (m < GPW) {
-                w0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg]);
-                w1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg + 4]);
-            }
+            // rows m < GPW of the bias operand carry group m's V biases (read for
+            // every lane, then zeroed by a select rather than a branch)
+            u32x4 w0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg]);
+            u32x4 w1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg + 4]);
+            if (m >= GPW) { w0 = (u32x4)0; w1 = (u32x4)0; }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int k = VB == 8 ? e : nib_order(e);
