@@ -151,7 +151,11 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
     int64_t S = (target_wg + items - 1) / items;
-    const int64_t min_steps_per_split = 1;
+    // two steps per split where that still leaves 128 workgroups: a workgroup's
+    // first step costs a full memory round trip, its second overlaps it
+    // (measured on 8 sequences x 2 KV heads over a 512-key window: 11.3 us at 9
+    // splits against 11.7 us at 18); below that, one step per split
+    const int64_t min_steps_per_split = items * ((steps + 1) / 2) >= 128 ? 2 : 1;
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
     const int forced = env_splits();
     if (forced > 0) S = forced;
