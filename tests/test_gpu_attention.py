@@ -86,7 +86,7 @@ def test_decode_split_invariance_and_determinism():
     lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
     outs = []
     try:
-        for s in ("1", "3", "16", "64"):
+        for s in ("1", "3", "16", "64", "128"):
             os.environ["KVQ_SPLITS"] = s
             outs.append(kvq.kvq_attn_decode(g, q, lens, L).clone())
         again = kvq.kvq_attn_decode(g, q, lens, L)
@@ -173,6 +173,34 @@ def test_shared_equals_separate_small():
     for i in range(3):
         ref = o.attend(small_q_bits(50 + i, (B, 8, D), 0.25)[:, :, None], lens_np)[:, :, 0]
         assert_close(torch_bf16_to_f64(outs[0][i]), ref, f"shared layer {i}")
+
+
+def test_shared_limits_four_groups_sixteen_layers():
+    """KVQ_MAX_SHARED_GROUPS groups in one call, one of them with
+    KVQ_MAX_SHARED_LAYERS layers (64 rows per KV head: four row tiles), mixed
+    head_dims (128 among them: one launch per descriptor), ragged lengths."""
+    B, L = 2, 700
+    specs = [  # Hkv, D, kb, vb, R, W, layers, Hq
+        (2, 256, 4, 4, 512, 300, kvq.MAX_SHARED_LAYERS, 8),
+        (1, 512, 8, 8, 1024, 0, 2, 8),
+        (2, 128, 8, 4, 256, 200, 3, 4),
+        (1, 256, 8, 8, 768, 0, 1, 4),
+    ]
+    assert len(specs) == kvq.MAX_SHARED_GROUPS
+    lens_np = np.array([L, L - 37], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    groups, refs = [], []
+    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(specs):
+        g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=200 + 10 * gi)
+        qs = [small_q_bits(300 + 10 * gi + l, (B, Hq, 1, D), D ** -0.25) for l in range(layers)]
+        groups.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens, L))
+        refs.append([o.attend(x, lens_np)[:, :, 0] for x in qs])
+    print("shared limits", flush=True)
+    outs = kvq.kvq_attn_decode_shared(groups)
+    torch.cuda.synchronize()
+    for gi in range(len(specs)):
+        for l, ref in enumerate(refs[gi]):
+            assert_close(torch_bf16_to_f64(outs[gi][l]), ref, f"group {gi} layer {l}")
 
 
 def test_shared_workload():
