@@ -34,8 +34,9 @@ SIZE_MAX = (1 << 64) - 1
 
 # Symbols include/kvq.h declares.
 EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
-           "kvq_attn_decode_shared", "kvq_decode_workspace_bytes", "kvq_decode_step_workspace_bytes",
-           "kvq_prefill_workspace_bytes", "kvq_last_error")
+           "kvq_attn_decode_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
+           "kvq_decode_step_workspace_bytes", "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
+           "kvq_last_error")
 
 
 class KvqUnavailable(RuntimeError):
@@ -64,6 +65,13 @@ class SharedGroupStruct(ctypes.Structure):
                 ("len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
 
 
+class ReadStruct(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(CacheStruct)), ("n_layers", ctypes.c_int32),
+                ("q", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_q_heads", ctypes.c_int32), ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -86,6 +94,10 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_decode_step_workspace_bytes.restype = sz
     lib.kvq_attn_prefill_chunk.argtypes = [CP, P, i32, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_attn_decode_shared.argtypes = [GP, i32, P, sz, P]
+    RP = ctypes.POINTER(ReadStruct)
+    lib.kvq_attn_mixed.argtypes = [RP, i32, P, sz, P]
+    lib.kvq_mixed_workspace_bytes.argtypes = [RP, i32]
+    lib.kvq_mixed_workspace_bytes.restype = sz
     lib.kvq_decode_workspace_bytes.argtypes = [GP, i32]
     lib.kvq_decode_workspace_bytes.restype = sz
     lib.kvq_prefill_workspace_bytes.argtypes = [CP, i32, i32, i32]
@@ -93,7 +105,7 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     for name in ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
-                 "kvq_attn_decode_shared"):
+                 "kvq_attn_decode_shared", "kvq_attn_mixed"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -304,3 +316,45 @@ def kvq_attn_decode_shared(groups: Sequence[SharedGroup], workspace: Optional[to
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.kvq_attn_decode_shared(arr, len(specs), _ptr(ws), wsb, _stream()))
     return [g.out for g in groups]
+
+
+@dataclass
+class Read:
+    """One read of a mixed launch: queries bf16 [B][Hq][chunk][D] per layer (chunk > 1: one layer)."""
+    cache: KVCache
+    q: List[torch.Tensor]
+    len: torch.Tensor
+    max_len: int
+    scale: float = 1.0
+    out: Optional[List[torch.Tensor]] = None
+
+
+def kvq_attn_mixed(reads: Sequence[Read], workspace: Optional[torch.Tensor] = None):
+    """Decode reads and short chunks in one attention launch; returns the per-read output lists."""
+    lib = load_library()
+    keep: list = []
+    structs = []
+    for r in reads:
+        for i, q in enumerate(r.q):
+            _gpu(q, f"q[{i}]", torch.bfloat16)
+            if q.dim() != 4:
+                raise ValueError("kvq_attn_mixed queries are [B][Hq][chunk][D]")
+        _gpu(r.len, "len", torch.int32)
+        if r.out is None:
+            r.out = [torch.empty_like(q) for q in r.q]
+        for i, o in enumerate(r.out):
+            _gpu(o, f"out[{i}]", torch.bfloat16)
+        qa = (ctypes.c_void_p * len(r.q))(*[_ptr(q) for q in r.q])
+        oa = (ctypes.c_void_p * len(r.out))(*[_ptr(o) for o in r.out])
+        cs = r.cache.struct
+        keep.extend([qa, oa, cs])
+        structs.append(ReadStruct(ctypes.pointer(cs), len(r.q), qa, oa, r.q[0].shape[1], r.q[0].shape[2],
+                                  float(r.scale), _ptr(r.len), int(r.max_len)))
+    arr = (ReadStruct * len(structs))(*structs)
+    nbytes = lib.kvq_mixed_workspace_bytes(arr, len(structs))
+    if nbytes == SIZE_MAX:
+        raise KvqError(1, "invalid arguments for kvq_mixed_workspace_bytes")
+    ws = _workspace(nbytes, workspace, reads[0].q[0].device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.kvq_attn_mixed(arr, len(structs), _ptr(ws), wsb, _stream()))
+    return [r.out for r in reads]

@@ -297,6 +297,34 @@ KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, c
     return ok();
 }
 
+// ReadSpecs of a mixed launch; a non-OK status (with a message) when a read is
+// invalid.  sizing: only what the workspace query can check (no pointers).
+static kvq_status mixed_specs(const kvq_read* reads, int32_t n, ReadSpec* rs, const char* what, bool sizing)
+{
+    if (!reads) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: reads is NULL", what);
+    if (n < 1 || n > KVQ_MAX_SHARED_GROUPS)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_reads %d outside [1, %d]", what, n, KVQ_MAX_SHARED_GROUPS);
+    for (int i = 0; i < n; ++i) {
+        const kvq_read& g = reads[i];
+        if (g.chunk < 1) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: read %d: chunk %d < 1", what, i, g.chunk);
+        if (g.chunk > 1 && g.n_layers != 1)
+            return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: read %d: a chunk of %d queries needs n_layers == 1",
+                        what, i, g.chunk);
+        rs[i] = ReadSpec{g.cache, g.n_layers, g.q, g.out, g.n_q_heads, g.scale, g.len, g.max_len, g.chunk};
+        kvq_status st;
+        if (sizing) {
+            st = check_cache(g.cache, what);
+            if (st == KVQ_OK && (g.n_layers < 1 || g.n_layers > KVQ_MAX_SHARED_LAYERS || g.n_q_heads < 1 ||
+                                 g.n_q_heads % g.cache->n_kv_heads != 0 || g.max_len < g.chunk))
+                st = KVQ_ERR_INVALID_ARGUMENT;
+        } else {
+            st = check_read(rs[i], what);
+        }
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
 KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_t n_groups)
 {
     if (!groups || n_groups < 1 || n_groups > KVQ_MAX_SHARED_GROUPS) return SIZE_MAX;
@@ -515,6 +543,25 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+KVQ_API size_t kvq_mixed_workspace_bytes(const kvq_read* reads, int32_t n_reads)
+{
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    if (mixed_specs(reads, n_reads, rs, "kvq_mixed_workspace_bytes", true) != KVQ_OK) return SIZE_MAX;
+    kvq::AttnParams P;
+    int total = 0;
+    return plan_all(rs, n_reads, P, total);
+}
+
+KVQ_API kvq_status kvq_attn_mixed(const kvq_read* reads, int32_t n_reads, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream)
+{
+    const char* what = "kvq_attn_mixed";
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    kvq_status st = mixed_specs(reads, n_reads, rs, what, false);
+    if (st != KVQ_OK) return st;
+    return run_reads(rs, n_reads, workspace, workspace_bytes, stream, what);
 }
 
 KVQ_API kvq_status kvq_attn_decode_shared(const kvq_shared_group* groups, int32_t n_groups,

@@ -212,6 +212,42 @@ kvq_status kvq_attn_decode_shared(const kvq_shared_group *groups, int32_t n_grou
                                   void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/*
+ * (host) One read of a mixed launch: like kvq_shared_group, plus the number of
+ * queries per sequence.  chunk == 1 is a decode read by n_layers layers; chunk
+ * > 1 is a short causal chunk (a speculative-verify window: query i of
+ * sequence b sits at len[b] - chunk + i, as for kvq_attn_prefill_chunk) read
+ * by one layer (n_layers == 1).
+ *   q[l], out[l]  bf16 [B][Hq][chunk][D]
+ * (page 80, model.ts: the decode and prompt phase declarations; reads of
+ * different caches at different positions and phases share one grid.)
+ */
+typedef struct {
+    const kvq_cache *cache;
+    int32_t n_layers;
+    const uint16_t *const *q;
+    uint16_t *const *out;
+    int32_t n_q_heads;
+    int32_t chunk;
+    float scale;
+    const int32_t *len;
+    int32_t max_len;
+} kvq_read;
+
+/*
+ * Decode reads and short chunks of different caches in one attention launch
+ * (plus one combine launch); each output equals that of the read alone
+ * (kvq_attn_decode, or kvq_attn_prefill_chunk of the chunk) up to rounding.
+ * 1 <= n_reads <= KVQ_MAX_SHARED_GROUPS; chunks run on the decode kernel, so a
+ * chunk's rows (chunk x Hq/Hkv per KV head) are read in 16-row tiles.
+ */
+kvq_status kvq_attn_mixed(const kvq_read *reads, int32_t n_reads,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* (host) Workspace bytes for kvq_attn_mixed with these reads (SIZE_MAX when invalid). */
+size_t kvq_mixed_workspace_bytes(const kvq_read *reads, int32_t n_reads);
+
 /* (host) Workspace bytes for kvq_attn_decode_shared with these groups; for a
  * kvq_attn_decode call pass one group with n_layers = 1.  Returns 0 when the
  * call needs none, and SIZE_MAX when the arguments are invalid. */

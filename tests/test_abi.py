@@ -124,3 +124,41 @@ def test_python_binding_refuses_cpu_tensors(lib):
     c = kvq.KVCache.__new__(kvq.KVCache)
     with pytest.raises(kvq.KvqUnavailable):
         kvq.kvq_append_quantize(c, torch.zeros(1, 1, 1, 128), torch.zeros(1, 1, 1, 128), torch.zeros(1, dtype=torch.int32))
+
+
+def mixed(lib, c, n_layers=1, chunk=1, Hq=8, max_len=600, n=1, ws=0):
+    qa = (ctypes.c_void_p * max(n_layers, 1))(*([FAKE] * max(n_layers, 1)))
+    r = kvq.ReadStruct(ctypes.pointer(c), n_layers, qa, qa, Hq, chunk, 1.0, FAKE, max_len)
+    arr = (kvq.ReadStruct * max(n, 1))(*([r] * max(n, 1)))
+    return lib.kvq_attn_mixed(arr, n, None, ws, None), lib.kvq_mixed_workspace_bytes(arr, n)
+
+
+def test_mixed_validation_and_workspace_query(lib):
+    st, nb = mixed(lib, cache(), n=0)
+    assert st == 1 and nb == kvq.SIZE_MAX
+    st, nb = mixed(lib, cache(), n=kvq.MAX_SHARED_GROUPS + 1)
+    assert st == 1 and nb == kvq.SIZE_MAX
+    st, nb = mixed(lib, cache(), chunk=0)                          # chunk < 1
+    assert st == 1 and nb == kvq.SIZE_MAX
+    st, nb = mixed(lib, cache(), chunk=4, n_layers=2)              # a chunk reads one layer
+    assert st == 1 and nb == kvq.SIZE_MAX
+    st, _ = mixed(lib, cache(), chunk=4)                           # window 512 + 4 - 1 > capacity 512
+    assert st == 3
+    st, nb = mixed(lib, cache(capacity=520), chunk=4)              # valid: needs a workspace
+    assert nb not in (0, kvq.SIZE_MAX) and st == 4
+    st, nb = mixed(lib, cache(capacity=520), n_layers=3)           # decode by three layers
+    assert nb not in (0, kvq.SIZE_MAX) and st == 4
+    assert lib.kvq_last_error().decode()
+
+
+def test_decode_step_validation(lib):
+    c = cache()
+    step = lambda k, v, Hq=8, ws=0: lib.kvq_decode_step(ctypes.byref(c), k, v, FAKE, Hq, FAKE, 600, 1.0, FAKE,
+                                                        None, ws, None)
+    assert step(None, FAKE) == 1                                   # k NULL
+    assert step(FAKE, FAKE + 4) == 1                               # v not 16-byte aligned
+    assert step(FAKE, FAKE, Hq=7) == 1                             # Hq % Hkv
+    assert step(FAKE, FAKE) == 4                                   # workspace too small
+    nb = lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 8, 600)
+    assert nb not in (0, kvq.SIZE_MAX)
+    assert lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 7, 600) == kvq.SIZE_MAX

@@ -325,3 +325,40 @@ def test_prefill_workload():
     o, _ = orc["kv"]
     mx, mean = assert_close(torch_bf16_to_f64(out), o.attend(q, lens), "prefill workload")
     print(f"prefill: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("with_d128", [False, True])
+def test_mixed_decode_and_verify_reads(with_d128):
+    """Decode reads (several layers) and short chunks of other caches in one
+    kvq_attn_mixed call, ragged lengths; with a head_dim 128 read the call falls
+    back to one launch per read, without it all reads share one launch."""
+    B, L = 2, 900
+    lens_np = np.array([L, L - 11], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    specs = [  # Hkv, D, kb, vb, R, W, layers, Hq, chunk
+        (2, 256, 4, 8, 520, 512, 3, 8, 1),
+        (1, 512, 8, 8, 1024, 0, 1, 8, 5),
+        (2, 256, 8, 4, 136, 128, 1, 16, 8),
+    ]
+    if with_d128:
+        specs.append((2, 128, 8, 4, 256, 200, 1, 4, 3))
+    reads, refs = [], []
+    for i, (Hkv, D, kb, vb, R, W, layers, Hq, C) in enumerate(specs):
+        g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=400 + 10 * i)
+        qs = [small_q_bits(500 + 10 * i + l, (B, Hq, C, D), D ** -0.25) for l in range(layers)]
+        reads.append(kvq.Read(g, [q_dev(x) for x in qs], lens, L))
+        refs.append([o.attend(x, lens_np) for x in qs])
+    print(f"mixed with_d128={with_d128}", flush=True)
+    outs = kvq.kvq_attn_mixed(reads)
+    torch.cuda.synchronize()
+    for i in range(len(specs)):
+        for l, ref in enumerate(refs[i]):
+            assert_close(torch_bf16_to_f64(outs[i][l]), ref, f"read {i} layer {l}")
+
+
+def test_mixed_rejects_multi_layer_chunk():
+    g = kvq.KVCache(1, 1, 256, 4, 4, 64)
+    q = torch.zeros(1, 8, 2, 256, dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((1,), 10, dtype=torch.int32, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_attn_mixed([kvq.Read(g, [q, q], lens, 10)])
