@@ -113,13 +113,15 @@ class Runner:
             cache_bytes += spec.B * spec.Hkv * spec.R * (spec.D * (spec.k_bits + spec.v_bits) // 8 + 8 * G)
         self.nrep = max(1, int(np.ceil(rotate_bytes / cache_bytes)))
         self.C = max(q.C for q in wl.queries)
+        # tokens each cache's step appends: the chunk of the queries that read it
+        self.C_of = {spec.name: max(q.C for q in wl.queries if q.cache == spec.name) for spec in wl.caches}
         dev = "cuda"
         self.caches = {spec.name: [kvq.KVCache(spec.B, spec.Hkv, spec.D, spec.k_bits, spec.v_bits, spec.R, spec.window)]
                        for spec in wl.caches}
         self.step_kv = {}
         self.oracle_chunks = {} if keep_oracle else None
         for spec in wl.caches:
-            new0 = spec.length - self.C
+            new0 = spec.length - self.C_of[spec.name]
             for pos, k, v in gen.kv_chunks(spec):
                 if keep_oracle:
                     self.oracle_chunks.setdefault(spec.name, []).append((pos, k, v))
@@ -145,12 +147,13 @@ class Runner:
         self.q = {}
         for qs, layers in zip(wl.queries, gen.q):
             t = [torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in layers]
-            if qs.C == 1:
+            if qs.C == 1 and wl.kind != "mixed":         # mixed reads take [B][Hq][C][D] queries
                 t = [x[:, :, 0].contiguous() for x in t]
             self.q[qs.cache] = t
         self.q_draws = gen.q
         self.len = {spec.name: torch.full((spec.B,), spec.length, dtype=torch.int32, device=dev) for spec in wl.caches}
-        self.pos_new = {spec.name: torch.full((spec.B,), spec.length - self.C, dtype=torch.int32, device=dev)
+        self.pos_new = {spec.name: torch.full((spec.B,), spec.length - self.C_of[spec.name], dtype=torch.int32,
+                                              device=dev)
                         for spec in wl.caches}
         self.out = {name: [torch.empty_like(x) for x in qs] for name, qs in self.q.items()}
         if wl.kind == "shared":
@@ -159,6 +162,11 @@ class Runner:
                             for qs in wl.queries] for r in range(self.nrep)]
             nbytes = kvq.kvq_decode_workspace_bytes(
                 [(g.cache, g.q, g.out, g.len, g.max_len, g.scale) for g in self.groups[0]])
+        elif wl.kind == "mixed":
+            self.reads = [[kvq.Read(self.caches[qs.cache][r], self.q[qs.cache], self.len[qs.cache],
+                                    wl.cache(qs.cache).length, 1.0, self.out[qs.cache])
+                           for qs in wl.queries] for r in range(self.nrep)]
+            nbytes = kvq.kvq_mixed_workspace_bytes(self.reads[0])
         elif wl.kind in ("prefill", "verify"):
             spec = wl.caches[0]
             nbytes = kvq.kvq_prefill_workspace_bytes(self.caches["kv"][0], wl.queries[0].Hq, self.C, spec.length)
@@ -184,6 +192,8 @@ class Runner:
         kvq, wl = self.kvq, self.wl
         if wl.kind == "shared":
             kvq.kvq_attn_decode_shared(self.groups[r], workspace=self.ws)
+        elif wl.kind == "mixed":
+            kvq.kvq_attn_mixed(self.reads[r], workspace=self.ws)
         elif wl.kind in ("prefill", "verify"):
             kvq.kvq_attn_prefill_chunk(self.caches["kv"][r], self.q["kv"][0], self.len["kv"], wl.caches[0].length,
                                        1.0, out=self.out["kv"][0], workspace=self.ws)
@@ -273,8 +283,8 @@ def cpu_baseline(wl, runner, budget_s=10.0):
         for spec in wl.caches:
             o, _ = caches[spec.name]
             pos, k, v = runner.oracle_chunks[spec.name][-1]
-            T = k.shape[2]
-            o.append(k[:nb, :, T - runner.C:], v[:nb, :, T - runner.C:], np.full(nb, spec.length - runner.C, np.int32))
+            T, C = k.shape[2], runner.C_of[spec.name]
+            o.append(k[:nb, :, T - C:], v[:nb, :, T - C:], np.full(nb, spec.length - C, np.int32))
         for qs, layers in zip(wl.queries, runner.q_draws):
             o, spec = caches[qs.cache]
             for x in layers:

@@ -9,8 +9,11 @@ Functions (same names as the C entry points):
   kvq_append_quantize(cache, k, v, pos0)
   kvq_attn_decode(cache, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_attn_prefill_chunk(cache, q, len, max_len, scale=1.0, out=None, workspace=None)
+  kvq_decode_step(cache, k, v, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_attn_decode_shared(groups, workspace=None)
-  kvq_decode_workspace_bytes(groups), kvq_prefill_workspace_bytes(...)
+  kvq_attn_mixed(reads, workspace=None)
+  kvq_decode_workspace_bytes(groups), kvq_decode_step_workspace_bytes(...),
+  kvq_mixed_workspace_bytes(reads), kvq_prefill_workspace_bytes(...)
 """
 from __future__ import annotations
 
@@ -329,11 +332,33 @@ class Read:
     out: Optional[List[torch.Tensor]] = None
 
 
+def kvq_mixed_workspace_bytes(reads: Sequence[Read]) -> int:
+    """Workspace bytes kvq_attn_mixed needs for these reads."""
+    keep: list = []
+    arr = _read_structs(reads, keep)
+    n = load_library().kvq_mixed_workspace_bytes(arr, len(reads))
+    if n == SIZE_MAX:
+        raise KvqError(1, "invalid arguments for kvq_mixed_workspace_bytes")
+    return n
+
+
+def _read_structs(reads: Sequence["Read"], keep: list):
+    structs = []
+    for r in reads:
+        outs = r.out if r.out is not None else r.q
+        qa = (ctypes.c_void_p * len(r.q))(*[_ptr(q) for q in r.q])
+        oa = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+        cs = r.cache.struct
+        keep.extend([qa, oa, cs])
+        structs.append(ReadStruct(ctypes.pointer(cs), len(r.q), qa, oa, r.q[0].shape[1], r.q[0].shape[2],
+                                  float(r.scale), _ptr(r.len), int(r.max_len)))
+    return (ReadStruct * len(structs))(*structs)
+
+
 def kvq_attn_mixed(reads: Sequence[Read], workspace: Optional[torch.Tensor] = None):
     """Decode reads and short chunks in one attention launch; returns the per-read output lists."""
     lib = load_library()
     keep: list = []
-    structs = []
     for r in reads:
         for i, q in enumerate(r.q):
             _gpu(q, f"q[{i}]", torch.bfloat16)
@@ -344,17 +369,11 @@ def kvq_attn_mixed(reads: Sequence[Read], workspace: Optional[torch.Tensor] = No
             r.out = [torch.empty_like(q) for q in r.q]
         for i, o in enumerate(r.out):
             _gpu(o, f"out[{i}]", torch.bfloat16)
-        qa = (ctypes.c_void_p * len(r.q))(*[_ptr(q) for q in r.q])
-        oa = (ctypes.c_void_p * len(r.out))(*[_ptr(o) for o in r.out])
-        cs = r.cache.struct
-        keep.extend([qa, oa, cs])
-        structs.append(ReadStruct(ctypes.pointer(cs), len(r.q), qa, oa, r.q[0].shape[1], r.q[0].shape[2],
-                                  float(r.scale), _ptr(r.len), int(r.max_len)))
-    arr = (ReadStruct * len(structs))(*structs)
-    nbytes = lib.kvq_mixed_workspace_bytes(arr, len(structs))
+    arr = _read_structs(reads, keep)
+    nbytes = lib.kvq_mixed_workspace_bytes(arr, len(reads))
     if nbytes == SIZE_MAX:
         raise KvqError(1, "invalid arguments for kvq_mixed_workspace_bytes")
     ws = _workspace(nbytes, workspace, reads[0].q[0].device)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib.kvq_attn_mixed(arr, len(structs), _ptr(ws), wsb, _stream()))
+    _check(lib.kvq_attn_mixed(arr, len(reads), _ptr(ws), wsb, _stream()))
     return [r.out for r in reads]

@@ -533,9 +533,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
 
     // Software pipeline over steps: iteration i runs QK of step i+1 and PV of
     // step i (independent, so their MFMA and VALU chains interleave), then one
-    // barrier, then the softmax of step i+1.  K codes are loaded two steps
-    // ahead of their QK and V codes one step ahead of their PV, into ping-pong
-    // register sets (no copies: a copy would wait for the load).  Loads are
+    // barrier, then the softmax of step i+1.  K and V codes are loaded two
+    // steps ahead into ping-pong register sets (no copies: a copy would wait
+    // for the load); a V set is refilled right after its PV, so the first two
+    // steps of both go out with q and a two-step split waits for memory once.
+    // Loads are
     // issued unconditionally with the step index clamped, so the wait counters
     // stay exact; past the end the last step is read again from L2.
     int last = max(nsteps - 1, 0);
@@ -550,6 +552,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     load_k(ka, stp(0));
     load_v(va, stp(0));
     load_k(kb, stp(1));
+    load_v(vb, stp(1));
     const int len_act = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
     if (len_act != P.max_len) {
         ranges(len_act);
@@ -560,6 +563,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             load_k(ka, stp(0));
             load_v(va, stp(0));
             load_k(kb, stp(1));
+            load_v(vb, stp(1));
         }
     }
     setup_q();
@@ -570,17 +574,17 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     }
     for (int i = 0; i < nsteps; i += 2) {
         load_k(ka, stp(i + 2));
-        load_v(vb, stp(i + 1));
         if (i + 1 < nsteps) qk(kb, 1);
         do_pv(va, st0 + i * kStep, p);
+        load_v(va, stp(i + 2));
         __syncthreads();
         if (i + 1 >= nsteps) break;
         do_softmax(st0 + (i + 1) * kStep, 1, p);
 
         load_k(kb, stp(i + 3));
-        load_v(va, stp(i + 2));
         if (i + 2 < nsteps) qk(ka, 0);
         do_pv(vb, st0 + (i + 1) * kStep, p);
+        load_v(vb, stp(i + 3));
         __syncthreads();
         if (i + 2 >= nsteps) break;
         do_softmax(st0 + (i + 2) * kStep, 0, p);

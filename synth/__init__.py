@@ -52,7 +52,7 @@ class QuerySpec:
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "decode" | "prefill" | "verify" (a few queries per sequence) | "shared"
+    kind: str            # "decode" | "prefill" | "verify" (a few queries per sequence) | "shared" | "mixed"
     caches: Tuple[CacheSpec, ...]
     queries: Tuple[QuerySpec, ...]
     seed: int = 0
@@ -98,6 +98,12 @@ WORKLOADS: Dict[str, Workload] = {
             [QuerySpec("kv", 1, 8, 5)],
             "speculative verify window on a full layer, B4, 5 queries per sequence, 8 q / 1 kv head, "
             "D512, K8/V8, cached length 32768"),
+        _wl("mixed_b8_decode_verify", "mixed",
+            [CacheSpec("donor", 8, 2, 256, 4, 8, 520, 512, 4096),
+             CacheSpec("full", 8, 1, 512, 8, 8, 16384, 0, 16384)],
+            [QuerySpec("donor", 3, 8), QuerySpec("full", 1, 8, 5)],
+            "mixed launch, B8: three layers decoding over a sliding cache (D256, K4/V8, window 512) "
+            "and a 5-token verify chunk over a full layer (D512, K8/V8, 16384 tokens), one attention launch"),
         _wl("shared_decode_b32", "shared",
             [CacheSpec("donor", 32, 2, 256, 4, 4, 512, 512, 16384),
              CacheSpec("full", 32, 1, 512, 8, 8, 16384, 0, 16384)],

@@ -224,6 +224,31 @@ def test_shared_workload():
     assert_close(torch_bf16_to_f64(outs[1][0])[sel], ref, "full layer")
 
 
+def test_mixed_workload():
+    """Three decoding layers over a sliding cache and a 5-token verify chunk over a
+    full D512 layer in one kvq_attn_mixed launch, against the oracle (full layer:
+    sampled batch rows)."""
+    wl = WORKLOADS["mixed_b8_decode_verify"]
+    sample = [0, 5, 7]
+    print("workload mixed_b8_decode_verify", flush=True)
+    gpu, orc, qd, _ = build_workload(wl, oracle_batches={"full": sample})
+    donor, full = wl.cache("donor"), wl.cache("full")
+    ld = torch.full((donor.B,), donor.length, dtype=torch.int32, device="cuda")
+    lf = torch.full((full.B,), full.length, dtype=torch.int32, device="cuda")
+    reads = [kvq.Read(gpu["donor"], [q_dev(x) for x in qd[0]], ld, donor.length),
+             kvq.Read(gpu["full"], [q_dev(x) for x in qd[1]], lf, full.length)]
+    kvq.kvq_attn_mixed(reads)
+    torch.cuda.synchronize()
+    od, _ = orc["donor"]
+    for i, x in enumerate(qd[0]):
+        assert_close(torch_bf16_to_f64(reads[0].out[i]), od.attend(x, np.full(donor.B, donor.length, np.int32)),
+                     f"donor layer {i}")
+    of, sel = orc["full"]
+    ref = of.attend(qd[1][0][sel], np.full(len(sel), full.length, np.int32))
+    mx, mean = assert_close(torch_bf16_to_f64(reads[1].out[0])[sel], ref, "full layer, 5-token chunk")
+    print(f"mixed full layer: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+
+
 PREFILL_CASES = [
     # B, Hq, Hkv, D, kb, vb, R, W, L, C
     (1, 8, 2, 256, 4, 4, 128, 100, 300, 29),
