@@ -9,11 +9,15 @@
 //
 // One workgroup holds all the rows of its (sequence, KV head), so every key is
 // read from HBM once per split; each 32-key step is dequantized into LDS once
-// and read by the 4 waves (16 rows each):
-//   * the 256 threads dequantize the step's K (token-major) and V (d-major) to
+// and read by every wave (4 row tiles of 16 rows):
+//   * all threads dequantize the step's K (token-major) and V (d-major) to
 //     fp16, x = code * scale + bias in one packed fp16 FMA per value pair;
 //   * each wave runs S^T = Khat Q^T and O^T = Vhat^T P^T on 16x16x32 fp16 MFMA
-//     from LDS, with the online softmax (base 2, lazy rescale).
+//     from LDS, with the online softmax (base 2, lazy rescale).  For D = 512 two
+//     waves share a row tile, each accumulating half of head_dim: both compute
+//     the tile's full scores (the same instructions on the same data, so the
+//     same softmax state), which keeps a wave's accumulators, q and in-flight
+//     codes within 256 registers and puts two waves on each SIMD.
 // Codes and scale|bias words are fetched two and three steps ahead; LDS holds
 // two steps; one barrier per step.  Rows follow the decode layout
 // (row = query * (Hq/Hkv) + head), so split partials go through the decode
@@ -25,9 +29,21 @@
 
 namespace kvq {
 
-constexpr int kCpWaves = 4;
-constexpr int kCpRows = kCpWaves * kRowTile;   // query rows per workgroup (kCodesPrefillRows)
+constexpr int kCpTiles = 4;                    // 16-row tiles per workgroup
+constexpr int kCpRows = kCpTiles * kRowTile;   // query rows per workgroup (kCodesPrefillRows)
 static_assert(kCpRows == kCodesPrefillRows, "host and kernel agree on the row block");
+
+template <int D>
+struct CpShape {
+    static constexpr int DH = D == 512 ? 2 : 1;   // waves per row tile (head_dim parts)
+    static constexpr int NW = kCpTiles * DH;      // waves per workgroup
+    static constexpr int NT = 64 * NW;            // threads
+    static constexpr int DW = D / DH;             // output columns of one wave
+    static constexpr int KCH = NT / kStep;        // K dequant: threads per key
+    static constexpr int CH = D / KCH;            // K values per thread
+    static constexpr int VD = D / NT;             // V dequant: head_dim columns per thread
+    static_assert(CH % 32 == 0 && CH <= 64 && VD >= 1 && NT * VD == D, "dequant assignment");
+};
 constexpr float kCpRescaleSlack = 8.0f;
 
 template <int D>
@@ -46,9 +62,9 @@ struct __attribute__((aligned(16))) CpSmem {
 
 template <int D, int KB, int VB>
 struct CpCodes {
-    // K: thread -> (key t/8, head_dim chunk t%8 of D/8 values); V: thread -> d (and d + 256)
-    static constexpr int KWT = D / 8 * KB / 32;          // K words per thread
-    static constexpr int VD = D / 256;                    // head_dim columns per thread
+    // K: thread -> (key t/KCH, head_dim chunk t%KCH of CH values); V: thread -> d (+ NT, ...)
+    static constexpr int KWT = CpShape<D>::CH * KB / 32;  // K words per thread
+    static constexpr int VD = CpShape<D>::VD;             // head_dim columns per thread
     static constexpr int VWT = VD * 4 * (VB / 4);         // V words per thread (4 blocks of 8 keys)
     uint32_t k[KWT];
     uint32_t v[VWT];
@@ -72,8 +88,10 @@ constexpr int cp_nset() { return D == 512 ? 3 : 4; }
 template <int D, int KB, int VB>
 __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>& sm)
 {
+    using Sh = CpShape<D>;
     constexpr int NSET = cp_nset<D, KB, VB>();
-    constexpr int G = D / 64, DT = D / 16, KS = D / 32;
+    constexpr int G = D / 64, KS = D / 32, NT = Sh::NT;
+    constexpr int DT = Sh::DW / 16;      // 16-column output tiles of this wave
     constexpr int KW = D * KB / 32;      // K words per slot
     constexpr int VW = VB / 4;           // V words per (block, d)
     using Codes = CpCodes<D, KB, VB>;
@@ -81,10 +99,13 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 15, lg = lane >> 4;
+    const int wtile = wave % kCpTiles;           // row tile of this wave
+    const int dh = wave / kCpTiles;              // head_dim part of this wave
+    const int dcol0 = dh * Sh::DW;               // its first output column
 
     // ---- work item: (b, kv head, 64-row block, split)
     const int S = P.S;
-    const int n_rb = (P.n_rt + kCpWaves - 1) / kCpWaves;
+    const int n_rb = (P.n_rt + kCpTiles - 1) / kCpTiles;
     const int s = idx % S;
     const int rb = (idx / S) % n_rb;
     const int bh = idx / (S * n_rb);
@@ -105,7 +126,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     const int st0 = j0 & ~(kStep - 1);
 
     // ---- this wave's 16 rows and this lane's row
-    const int rt = rb * kCpWaves + wave;                  // 16-row tile index
+    const int rt = rb * kCpTiles + wtile;                 // 16-row tile index
     const int wrow0 = rt * kRowTile;
     const bool wave_on = wrow0 < P.n_rows;
     const int wlast = min(wrow0 + kRowTile, P.n_rows) - 1;
@@ -126,7 +147,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     const uint32_t* __restrict__ vcodes = as_global(P.v_codes) + (int64_t)bh * (R / 8) * D * VW;
 
     // ---- loads of one step into registers
-    const int k_key = tid >> 3, k_chunk = tid & 7;        // K dequant assignment
+    const int k_key = tid / Sh::KCH, k_chunk = tid % Sh::KCH;   // K dequant assignment
     auto load_codes = [&](Codes& c, int st) {
         const int st_mod = st % R;
         const uint32_t* krow = kcodes + wrap_slot(st_mod + k_key, R) * KW + k_chunk * Codes::KWT;
@@ -140,7 +161,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
             const int vblk = wrap_slot(st_mod + 8 * blk, R) >> 3;
 #pragma unroll
             for (int dd = 0; dd < Codes::VD; ++dd) {
-                const uint32_t* vw = vcodes + ((int64_t)vblk * D + tid + 256 * dd) * VW;
+                const uint32_t* vw = vcodes + ((int64_t)vblk * D + tid + NT * dd) * VW;
                 if constexpr (VB == 8) {
                     const u32x2 x = *reinterpret_cast<const u32x2*>(vw);
                     c.v[(dd * 4 + blk) * 2] = x.x;
@@ -155,12 +176,12 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     constexpr int NSB = kStep * G;
     const int sb_key = tid % kStep, sb_g = tid / kStep;
     auto load_sb = [&](uint32_t (&w)[2], int st) {
-        const int o = NSB >= 256 || tid < NSB ? (int)(wrap_slot(st % R + sb_key, R) * G + (sb_g % G)) : 0;
+        const int o = NSB >= NT || tid < NSB ? (int)(wrap_slot(st % R + sb_key, R) * G + (sb_g % G)) : 0;
         w[0] = as_global(P.k_sb)[kslot0 * G + o];
         w[1] = as_global(P.v_sb)[kslot0 * G + o];
     };
     auto stage_sb = [&](const uint32_t (&w)[2], int slot) {
-        if (NSB >= 256 || tid < NSB) {
+        if (NSB >= NT || tid < NSB) {
             const int g = sb_g % G, key = sb_key;
             // V scale/bias go to the V^T element position of the key
             const int j = key & 7;
@@ -174,12 +195,12 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     // ---- dequantize one step into LDS buffer `slot`
     auto dequant = [&](const Codes& c, int slot) {
         {   // K: 8 values per code word (4-bit) / 4 (8-bit), one group per thread
-            const int g = (k_chunk * (D / 8)) / 64;
+            const int g = (k_chunk * Sh::CH) / 64;
             const uint32_t sw = sm.ks[slot][g][k_key], bw = sm.kb[slot][g][k_key];
             const f16x2 s2 = __builtin_bit_cast(f16x2, sw | (sw << 16));
             const f16x2 b2 = __builtin_bit_cast(f16x2, bw | (bw << 16));
             const int krow = 16 * ((k_key >> 2) & 1) + 4 * (k_key >> 3) + (k_key & 3);
-            _Float16* dst = &sm.kh[slot][krow][k_chunk * (D / 8)];
+            _Float16* dst = &sm.kh[slot][krow][k_chunk * Sh::CH];
 #pragma unroll
             for (int w = 0; w < Codes::KWT; w += (KB == 8 ? 2 : 1)) {
                 f16x2 pr[4];
@@ -200,7 +221,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
         }
 #pragma unroll
         for (int dd = 0; dd < Codes::VD; ++dd) {   // V: this thread's column d, 32 keys
-            const int d = tid + 256 * dd;
+            const int d = tid + NT * dd;
             const int g = d / 64;
             _Float16* dst = &sm.vt[slot][d][0];
 #pragma unroll
@@ -297,7 +318,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
         for (int e = 0; e < 8; ++e) pb[e] = (_Float16)p[VB == 8 ? e : nib_order(e)];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.vt[slot][16 * dt + m][8 * lg]);
+            const f16x8 a = *reinterpret_cast<const f16x8*>(&sm.vt[slot][dcol0 + 16 * dt + m][8 * lg]);
             O[dt] = mfma_f16(a, pb, O[dt]);
         }
     };
@@ -351,7 +372,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     // ---- write this wave's rows
     if (!wave_on || !row_ok) return;
     const float L = sum_across_groups(l_run);
-    const int dcol = 4 * lg;
+    const int dcol = dcol0 + 4 * lg;
     if (S == 1) {
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
         uint16_t* orow = as_global(P.out[0]) + ((((int64_t)b * P.Hq + hq) * C + qi) * D);
@@ -369,7 +390,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
         float* po = as_global(P.part) + prow * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
-        if (lg == 0) {
+        if (lg == 0 && dh == 0) {
             float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
             pml[0] = m_run;
             pml[1] = L;
@@ -378,7 +399,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
 }
 
 template <int D, int KB, int VB>
-__global__ __launch_bounds__(256) void codes_prefill_kernel(AttnParams P)
+__global__ __launch_bounds__(CpShape<D>::NT) void codes_prefill_kernel(AttnParams P)
 {
     __shared__ CpSmem<D> sm;
     codes_body<D, KB, VB>(P.d[0], blockIdx.x, sm);
@@ -386,11 +407,11 @@ __global__ __launch_bounds__(256) void codes_prefill_kernel(AttnParams P)
 
 hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_t stream)
 {
-    const dim3 grid(total_items), block(256);
+    const dim3 grid(total_items);
     switch (p.d[0].cfg) {
 #define KVQ_CP(D_, KB_, VB_) \
     case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
-        codes_prefill_kernel<D_, KB_, VB_><<<grid, block, 0, stream>>>(p); break;
+        codes_prefill_kernel<D_, KB_, VB_><<<grid, dim3(CpShape<D_>::NT), 0, stream>>>(p); break;
     KVQ_CP(256, 4, 4) KVQ_CP(256, 4, 8) KVQ_CP(256, 8, 4) KVQ_CP(256, 8, 8)
     KVQ_CP(512, 4, 4) KVQ_CP(512, 4, 8) KVQ_CP(512, 8, 4) KVQ_CP(512, 8, 8)
 #undef KVQ_CP
