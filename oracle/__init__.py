@@ -13,6 +13,8 @@ Layouts here are the plain ones:
   codes   uint8  [B][H][R][D]         one code per byte
   scales  uint16 [B][H][R][D/64]      bf16 bit patterns
   biases  uint16 [B][H][R][D/64]
+  a side of width 16 (an unquantized bf16 cache, the pages' bf16 sliding layers):
+  vals    uint16 [B][H][R][D]         bf16 bit patterns, nearest-even rounding
 """
 from __future__ import annotations
 
@@ -70,6 +72,13 @@ def _load():
         lib.kvqo_attend.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                     P, i32, i32, P, ctypes.c_double, P, i32]
         lib.kvqo_attend.restype = i32
+        lib.kvqo_attend_any.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                        P, i32, i32, P, ctypes.c_double, P, i32]
+        lib.kvqo_attend_any.restype = i32
+        lib.kvqo_append_bf16.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        lib.kvqo_append_bf16.restype = i32
+        lib.kvqo_bf16.argtypes = [ctypes.c_float]
+        lib.kvqo_bf16.restype = ctypes.c_uint16
         lib.kvqo_max_threads.argtypes = []
         lib.kvqo_max_threads.restype = i32
         _lib = lib
@@ -96,8 +105,17 @@ def quantize_group(x, bits: int):
     return codes, int(s[0]), int(b[0])
 
 
+def bf16(x) -> int:
+    """One fp32 value rounded to the nearest bf16, ties to even (bit pattern)."""
+    h = int(_load().kvqo_bf16(float(np.float32(x))))
+    if h == 0xFFFF:
+        raise OracleError(1, "bf16")
+    return h
+
+
 class Cache:
-    """A plain-layout quantized cache for one layer (K and V, each with its own width)."""
+    """A plain-layout cache for one layer, K and V each with its own width: 4 or 8
+    (affine codes, scales, biases) or 16 (bf16 values, unquantized)."""
 
     def __init__(self, B: int, H: int, D: int, R: int, k_bits: int, v_bits: int, window: int = 0):
         if D % GROUP:
@@ -111,18 +129,25 @@ class Cache:
         self.k_biases = np.zeros((B, H, R, G), np.uint16)
         self.v_scales = np.zeros((B, H, R, G), np.uint16)
         self.v_biases = np.zeros((B, H, R, G), np.uint16)
+        self.k_vals = np.zeros((B, H, R, D), np.uint16) if k_bits == 16 else None
+        self.v_vals = np.zeros((B, H, R, D), np.uint16) if v_bits == 16 else None
 
     def append(self, k, v, pos0):
-        """Quantize-and-append T tokens: k, v fp32 [B][H][T][D]; pos0 [B]."""
+        """Quantize-and-append (or, for a 16-bit side, round-and-append) T tokens:
+        k, v fp32 [B][H][T][D]; pos0 [B]."""
         k = np.ascontiguousarray(k, dtype=np.float32)
         v = np.ascontiguousarray(v, dtype=np.float32)
         pos0 = np.ascontiguousarray(pos0, dtype=np.int32)
         B, H, T, D = k.shape
         assert (B, H, D) == (self.B, self.H, self.D) and v.shape == k.shape
         lib = _load()
-        for x, bits, c, s, b, what in ((k, self.k_bits, self.k_codes, self.k_scales, self.k_biases, "K"),
-                                       (v, self.v_bits, self.v_codes, self.v_scales, self.v_biases, "V")):
-            st = lib.kvqo_append(_ptr(x), B, H, T, D, bits, self.R, _ptr(pos0), _ptr(c), _ptr(s), _ptr(b))
+        for x, bits, c, s, b, vals, what in (
+                (k, self.k_bits, self.k_codes, self.k_scales, self.k_biases, self.k_vals, "K"),
+                (v, self.v_bits, self.v_codes, self.v_scales, self.v_biases, self.v_vals, "V")):
+            if bits == 16:
+                st = lib.kvqo_append_bf16(_ptr(x), B, H, T, D, self.R, _ptr(pos0), _ptr(vals))
+            else:
+                st = lib.kvqo_append(_ptr(x), B, H, T, D, bits, self.R, _ptr(pos0), _ptr(c), _ptr(s), _ptr(b))
             if st:
                 raise OracleError(st, f"append {what}")
 
@@ -131,9 +156,13 @@ class Cache:
         return pack_words(self.k_codes, self.k_bits)
 
     def dequant_k(self):
+        if self.k_vals is not None:
+            return bf16_values(self.k_vals)
         return dequant(self.k_codes, self.k_scales, self.k_biases)
 
     def dequant_v(self):
+        if self.v_vals is not None:
+            return bf16_values(self.v_vals)
         return dequant(self.v_codes, self.v_scales, self.v_biases)
 
     def attend(self, q_bits, len_, scale: float = 1.0, nthreads: int = 0):
@@ -143,9 +172,11 @@ class Cache:
         B, Hq, C, D = q_bits.shape
         assert B == self.B and D == self.D
         out = np.zeros((B, Hq, C, D), np.float64)
-        st = _load().kvqo_attend(
-            _ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.k_biases),
-            _ptr(self.v_codes), _ptr(self.v_scales), _ptr(self.v_biases),
+        kv = None if self.k_vals is None else _ptr(self.k_vals)
+        vv = None if self.v_vals is None else _ptr(self.v_vals)
+        st = _load().kvqo_attend_any(
+            _ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.k_biases), kv,
+            _ptr(self.v_codes), _ptr(self.v_scales), _ptr(self.v_biases), vv,
             B, self.H, D, self.R, self.window, _ptr(q_bits), Hq, C, _ptr(len_),
             float(scale), _ptr(out), int(nthreads))
         if st:
@@ -170,6 +201,12 @@ def dequant(codes, scales, biases):
     out = np.zeros(codes.shape, np.float64)
     _load().kvqo_dequant(_ptr(codes), _ptr(scales), _ptr(biases), codes.size // D, D, _ptr(out))
     return out
+
+
+def bf16_values(vals):
+    """bf16 bit patterns -> fp64 values (exact)."""
+    vals = np.ascontiguousarray(vals, dtype=np.uint16)
+    return (vals.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def attend_shared(cache: Cache, q_layers, len_, scale: float = 1.0, nthreads: int = 0):

@@ -25,6 +25,13 @@
  * fused multiply-add (build with -ffp-contract=off); dequantization and
  * attention run in fp64.
  *
+ * A layer's cache may instead hold bf16 values, unquantized: the pages keep
+ * the sliding layers' caches in bf16 under the other KV scheme they compose
+ *   [p80 model.ts cacheLayers note]  sliding layers compose a ring of the window
+ *                                and stay bf16; the full layers' read is deferred.
+ * Such a cache stores each fp32 key or value rounded to the nearest bf16 (ties
+ * to even), and its read uses those values exactly.
+ *
  * Status codes: 0 ok, 1 invalid argument (bad bits/shape, non-finite or
  * out-of-domain input), 2 capacity (the cache cannot hold every key a query
  * must see).
@@ -152,6 +159,58 @@ int kvqo_append(const float *x, int B, int H, int T, int D, int bits, int R,
     return 0;
 }
 
+/* The bf16 value nearest to x (finite, |x| <= KVQO_MAX_ABS), ties to the one
+ * whose last mantissa bit is 0.  The two candidates are x with its low 16 bits
+ * dropped (toward zero) and the next bf16 value away from zero; their distances
+ * to x are exact in fp64. */
+static uint16_t bf16_nearest_even(float x)
+{
+    const uint32_t u = bits_of(x);
+    const uint32_t toward = u & 0xFFFF0000u;
+    if (toward == u) return (uint16_t)(u >> 16);
+    const uint32_t away = toward + 0x10000u;
+    const double d_toward = fabs((double)x - (double)float_of(toward));
+    const double d_away = fabs((double)float_of(away) - (double)x);
+    uint32_t r;
+    if (d_toward < d_away) r = toward;
+    else if (d_away < d_toward) r = away;
+    else r = ((toward >> 16) & 1u) ? away : toward;
+    return (uint16_t)(r >> 16);
+}
+
+/* One fp32 value rounded to bf16 as above (bit pattern); 0xFFFF flags an input
+ * outside the domain (non-finite or |x| > KVQO_MAX_ABS). */
+uint16_t kvqo_bf16(float x)
+{
+    if (!(fabsf(x) <= KVQO_MAX_ABS)) return 0xFFFFu;
+    return bf16_nearest_even(x);
+}
+
+/* Append T new tokens per sequence to an unquantized bf16 cache of R slots
+ * [p80 model.ts cacheLayers note: sliding layers stay bf16]:
+ *   x     fp32 [B][H][T][D]
+ *   vals  bf16 bits [B][H][R][D]
+ * with the slots, the ring and the T > R rule of kvqo_append. */
+int kvqo_append_bf16(const float *x, int B, int H, int T, int D, int R,
+                     const int32_t *pos0, uint16_t *vals)
+{
+    if (B < 0 || H <= 0 || T < 0 || D <= 0 || R <= 0) return 1;
+    for (int b = 0; b < B; ++b) if (pos0[b] < 0) return 1;
+    const int64_t total = (int64_t)B * H * T * D;
+    for (int64_t i = 0; i < total; ++i)
+        if (!(fabsf(x[i]) <= KVQO_MAX_ABS)) return 1;
+    const int first = T > R ? T - R : 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = first; t < T; ++t) {
+                const int64_t slot = ((int64_t)pos0[b] + t) % R;
+                const float *src = x + (((int64_t)b * H + h) * T + t) * D;
+                uint16_t *dst = vals + (((int64_t)b * H + h) * R + slot) * D;
+                for (int d = 0; d < D; ++d) dst[d] = bf16_nearest_even(src[d]);
+            }
+    return 0;
+}
+
 /* Pack unpacked codes row by row into little-endian uint32 words: word w of a
  * row holds elements [w*k, (w+1)*k) with k = 32/bits, element e at bits
  * [bits*(e mod k), bits*(e mod k + 1)). */
@@ -182,7 +241,25 @@ void kvqo_dequant(const uint8_t *codes, const uint16_t *scales, const uint16_t *
         }
 }
 
-/* Scaled-dot-product attention over a quantized cache, in fp64
+/* One side (K or V) of a cache as the attention reads it: affine codes with a
+ * bf16 scale and bias per group, or (bf16 != NULL) bf16 values. */
+typedef struct {
+    const uint8_t *codes;
+    const uint16_t *scales, *biases;
+    const uint16_t *bf16;
+} kvqo_side;
+
+/* Element d of cache row `row`, in fp64: code * scale + bias (exact), or the
+ * stored bf16 value. */
+static double side_value(const kvqo_side *s, int64_t row, int D, int d)
+{
+    if (s->bf16) return bf16_to_double(s->bf16[row * D + d]);
+    const int G = D / KVQO_GROUP;
+    return (double)s->codes[row * D + d] * bf16_to_double(s->scales[row * G + d / KVQO_GROUP])
+         + bf16_to_double(s->biases[row * G + d / KVQO_GROUP]);
+}
+
+/* Scaled-dot-product attention over a cache, in fp64
  * [p80 model.ts attentionTraining: read.attend(q, 1.0); header: SDPA scale 1.0].
  *   q    bf16 bits [B][Hq][C][D]; query i of sequence b sits at absolute
  *        position p = len[b] - C + i (the C new tokens were appended first)
@@ -196,15 +273,13 @@ void kvqo_dequant(const uint8_t *codes, const uint16_t *scales, const uint16_t *
  * the call fails with 2.
  *   z_j = scale * sum_d q_d * khat_{j,d};  w_j = exp(z_j - max z);
  *   out_d = sum_j w_j * vhat_{j,d} / sum_j w_j. */
-int kvqo_attend(const uint8_t *k_codes, const uint16_t *k_scales, const uint16_t *k_biases,
-                const uint8_t *v_codes, const uint16_t *v_scales, const uint16_t *v_biases,
-                int B, int Hkv, int D, int R, int W,
-                const uint16_t *q, int Hq, int C, const int32_t *len,
-                double scale, double *out, int nthreads)
+static int attend(const kvqo_side *ks, const kvqo_side *vs,
+                  int B, int Hkv, int D, int R, int W,
+                  const uint16_t *q, int Hq, int C, const int32_t *len,
+                  double scale, double *out, int nthreads)
 {
     if (B < 0 || Hkv <= 0 || D <= 0 || D % KVQO_GROUP != 0 || R <= 0 || W < 0) return 1;
     if (Hq <= 0 || Hq % Hkv != 0 || C <= 0) return 1;
-    const int G = D / KVQO_GROUP;
     const int per_kv = Hq / Hkv;
     for (int b = 0; b < B; ++b) {
         if (len[b] < C) return 1;
@@ -237,11 +312,7 @@ int kvqo_attend(const uint8_t *k_codes, const uint16_t *k_scales, const uint16_t
         for (int64_t j = lo; j <= p; ++j) {
             const int64_t kr = ((int64_t)b * Hkv + hkv) * R + j % R;
             double acc = 0.0;
-            for (int d = 0; d < D; ++d) {
-                const double kh = (double)k_codes[kr * D + d] * bf16_to_double(k_scales[kr * G + d / KVQO_GROUP])
-                                + bf16_to_double(k_biases[kr * G + d / KVQO_GROUP]);
-                acc += bf16_to_double(qrow[d]) * kh;
-            }
+            for (int d = 0; d < D; ++d) acc += bf16_to_double(qrow[d]) * side_value(ks, kr, D, d);
             z[j - lo] = scale * acc;
             if (z[j - lo] > zmax) zmax = z[j - lo];
         }
@@ -251,16 +322,39 @@ int kvqo_attend(const uint8_t *k_codes, const uint16_t *k_scales, const uint16_t
             const double w = exp(z[j - lo] - zmax);
             wsum += w;
             const int64_t vr = ((int64_t)b * Hkv + hkv) * R + j % R;
-            for (int d = 0; d < D; ++d) {
-                const double vh = (double)v_codes[vr * D + d] * bf16_to_double(v_scales[vr * G + d / KVQO_GROUP])
-                                + bf16_to_double(v_biases[vr * G + d / KVQO_GROUP]);
-                o[d] += w * vh;
-            }
+            for (int d = 0; d < D; ++d) o[d] += w * side_value(vs, vr, D, d);
         }
         for (int d = 0; d < D; ++d) o[d] /= wsum;
         free(z);
     }
     return status;
+}
+
+/* Attention over an affine-quantized cache (plain layouts of kvqo_append). */
+int kvqo_attend(const uint8_t *k_codes, const uint16_t *k_scales, const uint16_t *k_biases,
+                const uint8_t *v_codes, const uint16_t *v_scales, const uint16_t *v_biases,
+                int B, int Hkv, int D, int R, int W,
+                const uint16_t *q, int Hq, int C, const int32_t *len,
+                double scale, double *out, int nthreads)
+{
+    const kvqo_side ks = {k_codes, k_scales, k_biases, NULL};
+    const kvqo_side vs = {v_codes, v_scales, v_biases, NULL};
+    return attend(&ks, &vs, B, Hkv, D, R, W, q, Hq, C, len, scale, out, nthreads);
+}
+
+/* The same over any mix of sides: a side whose *_bf16 pointer is not NULL is
+ * read as bf16 values [B][H][R][D] (kvqo_append_bf16), the other as codes. */
+int kvqo_attend_any(const uint8_t *k_codes, const uint16_t *k_scales, const uint16_t *k_biases,
+                    const uint16_t *k_bf16,
+                    const uint8_t *v_codes, const uint16_t *v_scales, const uint16_t *v_biases,
+                    const uint16_t *v_bf16,
+                    int B, int Hkv, int D, int R, int W,
+                    const uint16_t *q, int Hq, int C, const int32_t *len,
+                    double scale, double *out, int nthreads)
+{
+    const kvqo_side ks = {k_codes, k_scales, k_biases, k_bf16};
+    const kvqo_side vs = {v_codes, v_scales, v_biases, v_bf16};
+    return attend(&ks, &vs, B, Hkv, D, R, W, q, Hq, C, len, scale, out, nthreads);
 }
 
 /* Threads an OpenMP region would use (1 without OpenMP). */
