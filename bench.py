@@ -20,7 +20,8 @@ bounded sample of the same workload; `configs` holds the same figures for
 every workload.
 
 Algorithmic bytes per visible (key, KV head): K and V codes plus one bf16
-scale and one bf16 bias per 64-group for K and for V; a donor cache read by
+scale and one bf16 bias per 64-group for K and for V (an unquantized bf16
+cache: its 2-byte K and V values, no scale or bias); a donor cache read by
 several layers counts once; plus the bf16 queries read and outputs written.
 Prefill is reported in TFLOP/s: 4*head_dim FLOPs per visible (query, key) pair.
 """
@@ -84,7 +85,7 @@ def algorithmic(wl):
     """(bytes, flops) of one read of the workload, per the formula in the module docstring."""
     byts, flops = 0, 0
     for spec in wl.caches:
-        per_key = spec.D * (spec.k_bits + spec.v_bits) // 8 + (spec.D // 64) * 8
+        per_key = spec.D * (spec.k_bits + spec.v_bits) // 8 + (0 if spec.k_bits == 16 else (spec.D // 64) * 8)
         qs = [q for q in wl.queries if q.cache == spec.name]
         C = max(q.C for q in qs)
         first = spec.length - C
@@ -142,7 +143,8 @@ class Runner:
             for _ in range(self.nrep - 1):
                 g = kvq.KVCache(spec.B, spec.Hkv, spec.D, spec.k_bits, spec.v_bits, spec.R, spec.window, zero=False)
                 for a, b in ((g.k_codes, g0.k_codes), (g.v_codes, g0.v_codes), (g.k_sb, g0.k_sb), (g.v_sb, g0.v_sb)):
-                    a.copy_(b)
+                    if a is not None:
+                        a.copy_(b)
                 self.caches[spec.name].append(g)
         self.q = {}
         for qs, layers in zip(wl.queries, gen.q):
@@ -174,12 +176,13 @@ class Runner:
             spec = wl.caches[0]
             g = self.caches["kv"][0]
             nbytes = kvq.kvq_decode_workspace_bytes([(g, self.q["kv"], self.out["kv"], self.len["kv"], spec.length, 1.0)])
-            nbytes = max(nbytes, kvq.kvq_decode_step_workspace_bytes(g, wl.queries[0].Hq, spec.length))
+            if spec.k_bits != 16:                 # the fused step takes quantized caches only
+                nbytes = max(nbytes, kvq.kvq_decode_step_workspace_bytes(g, wl.queries[0].Hq, spec.length))
             k, v = self.step_kv["kv"]
             self.step_k1 = k.reshape(spec.B, spec.Hkv, spec.D)
             self.step_v1 = v.reshape(spec.B, spec.Hkv, spec.D)
         # decode steps run as one fused call (append + read); the others as two
-        self.fused = wl.kind == "decode"
+        self.fused = wl.kind == "decode" and wl.caches[0].k_bits != 16
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 

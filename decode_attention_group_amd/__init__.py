@@ -143,6 +143,8 @@ class KVCache:
     k_codes int32 [B][H][R][D*k_bits/32]     (uint32 words)
     v_codes int32 [B][H][R/8][D][v_bits/4]   (uint32 words)
     k_sb, v_sb int32 [B][H][R][D/64]         (bf16 scale | bf16 bias << 16)
+    k_bits == v_bits == 16: an unquantized bf16 cache, the same layouts holding
+    bf16 values; no k_sb / v_sb (None).
     """
 
     def __init__(self, batch: int, n_kv_heads: int, head_dim: int, k_bits: int, v_bits: int,
@@ -153,21 +155,24 @@ class KVCache:
         alloc = torch.zeros if zero else torch.empty
         self.k_codes = alloc((B, H, R, D * k_bits // 32), dtype=torch.int32, device=device)
         self.v_codes = alloc((B, H, R // V_BLOCK, D, v_bits // 4), dtype=torch.int32, device=device)
-        self.k_sb = alloc((B, H, R, D // GROUP_SIZE), dtype=torch.int32, device=device)
-        self.v_sb = alloc((B, H, R, D // GROUP_SIZE), dtype=torch.int32, device=device)
+        if k_bits == 16:
+            self.k_sb = self.v_sb = None
+        else:
+            self.k_sb = alloc((B, H, R, D // GROUP_SIZE), dtype=torch.int32, device=device)
+            self.v_sb = alloc((B, H, R, D // GROUP_SIZE), dtype=torch.int32, device=device)
         self._struct = None
 
     @property
     def struct(self) -> CacheStruct:
         if self._struct is None:
             self._struct = CacheStruct(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
-                                       self.k_sb.data_ptr(), self.v_sb.data_ptr(),
+                                       _ptr(self.k_sb) or 0, _ptr(self.v_sb) or 0,
                                        self.batch, self.n_kv_heads, self.head_dim, GROUP_SIZE,
                                        self.k_bits, self.v_bits, self.capacity, self.window)
         return self._struct
 
     def nbytes(self) -> int:
-        return sum(t.numel() * 4 for t in (self.k_codes, self.v_codes, self.k_sb, self.v_sb))
+        return sum(t.numel() * 4 for t in (self.k_codes, self.v_codes, self.k_sb, self.v_sb) if t is not None)
 
 
 def kvq_append_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: torch.Tensor):
@@ -258,7 +263,11 @@ def kvq_decode_step(cache: KVCache, k: torch.Tensor, v: torch.Tensor, q: torch.T
     if out is None:
         out = torch.empty_like(q)
     _gpu(out, "out", torch.bfloat16)
-    nbytes = kvq_decode_step_workspace_bytes(cache, q.shape[1], max_len)
+    nbytes = lib.kvq_decode_step_workspace_bytes(ctypes.byref(cache.struct), q.shape[1], max_len)
+    if nbytes == SIZE_MAX:      # invalid or unsupported: the call itself reports why
+        _check(lib.kvq_decode_step(ctypes.byref(cache.struct), _ptr(k), _ptr(v), _ptr(q), q.shape[1], _ptr(len_),
+                                   int(max_len), float(scale), _ptr(out), None, 0, _stream()))
+        raise KvqError(1, "invalid arguments for kvq_decode_step")
     ws = _workspace(nbytes, workspace, q.device)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.kvq_decode_step(ctypes.byref(cache.struct), _ptr(k), _ptr(v), _ptr(q), q.shape[1], _ptr(len_),

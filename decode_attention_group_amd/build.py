@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["append.hip", "attn.hip", "prefill.hip", "prefill_codes.hip", "kvq_api.hip"]
+SOURCES = ["append.hip", "attn.hip", "prefill.hip", "prefill_codes.hip", "bf16_cache.hip", "kvq_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -41,18 +41,23 @@ bool trace_on()
 kvq_status check_cache(const kvq_cache* c, const char* what)
 {
     if (!c) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: cache descriptor is NULL", what);
-    if (!c->k_codes || !c->v_codes || !c->k_sb || !c->v_sb)
+    const bool bf16 = c->k_bits == 16 && c->v_bits == 16;
+    if (!c->k_codes || !c->v_codes || (!bf16 && (!c->k_sb || !c->v_sb)))
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: a cache array pointer is NULL", what);
     if (c->group_size != KVQ_GROUP_SIZE)
         return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (only 64 is supported)", what, c->group_size);
     if (c->head_dim != 128 && c->head_dim != 256 && c->head_dim != 512)
         return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256, 512)", what, c->head_dim);
-    if ((c->k_bits != 4 && c->k_bits != 8) || (c->v_bits != 4 && c->v_bits != 8))
-        return fail(KVQ_ERR_UNSUPPORTED, "%s: k_bits %d / v_bits %d (each must be 4 or 8)", what, c->k_bits, c->v_bits);
+    if (!bf16 && ((c->k_bits != 4 && c->k_bits != 8) || (c->v_bits != 4 && c->v_bits != 8)))
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: k_bits %d / v_bits %d (each 4 or 8, or both 16)", what, c->k_bits,
+                    c->v_bits);
     if (c->batch < 1 || c->n_kv_heads < 1)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d and n_kv_heads %d must be >= 1", what, c->batch, c->n_kv_heads);
-    if (c->capacity < KVQ_V_BLOCK || c->capacity % KVQ_V_BLOCK != 0)
-        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d must be a positive multiple of 8", what, c->capacity);
+    // a read loads the slots of a 32-key step as (step start mod R) + k, k < 32,
+    // wrapped with one subtraction: in range for R >= 32
+    if (c->capacity < KVQ_MIN_CAPACITY || c->capacity % KVQ_V_BLOCK != 0)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d must be a multiple of 8 and at least %d", what,
+                    c->capacity, KVQ_MIN_CAPACITY);
     if (c->window < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: window %d < 0", what, c->window);
     if (c->window > c->capacity)
         return fail(KVQ_ERR_CAPACITY, "%s: window %d exceeds capacity %d", what, c->window, c->capacity);
@@ -229,16 +234,22 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     bool same = true, big = true;
     for (int i = 0; i < n; ++i) {
         same &= P.d[i].cfg == P.d[0].cfg;
-        big &= P.d[i].D >= 256;
+        big &= P.d[i].D >= 256 && !kvq::cfg_is_bf16(P.d[i].cfg);
     }
+    auto launch_one = [&](const kvq::AttnParams& p, int items) {
+        return kvq::cfg_is_bf16(p.d[0].cfg) ? kvq::launch_attn_bf16(p, items, stream)
+                                            : kvq::launch_attn(p, items, false, stream);
+    };
     if (trace_on())
         for (int i = 0; i < n; ++i)
             fprintf(stderr, "[kvq] %s desc %d: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d tiles=%d S=%d split=%d wg=%d\n",
                     what, i, P.d[i].B, P.d[i].Hkv, P.d[i].Hq, P.d[i].D, P.d[i].R, P.d[i].W, P.d[i].C,
                     P.d[i].n_rows, P.d[i].n_rt, P.d[i].S, P.d[i].split_len, P.d[i].n_items);
     hipError_t e = hipSuccess;
-    if (same || big) {
-        e = kvq::launch_attn(P, total_items, !same, stream);
+    if (same) {
+        e = launch_one(P, total_items);
+    } else if (big) {
+        e = kvq::launch_attn(P, total_items, true, stream);
     } else {
         // Mixed configurations outside the fused set: one launch per descriptor.
         for (int i = 0; i < n && e == hipSuccess; ++i) {
@@ -247,7 +258,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
             one.n_desc = 1;
             one.d[0] = P.d[i];
             one.d[0].item_begin = 0;
-            e = kvq::launch_attn(one, P.d[i].n_items, false, stream);
+            e = launch_one(one, P.d[i].n_items);
         }
     }
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
@@ -289,6 +300,13 @@ KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, c
     p.n_written = T - p.t_first;
     const int n_cand = std::min(p.R / 8, (p.n_written + 7) / 8 + 1);
     if (2 * (int64_t)p.B > 65535) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d too large", what, p.B);
+    if (cache->k_bits == 16) {                    // bf16 cache: round and store, no quantizer
+        if (trace_on())
+            fprintf(stderr, "[kvq] %s (bf16): B=%d H=%d T=%d D=%d R=%d\n", what, p.B, p.H, T, p.D, p.R);
+        const hipError_t e = kvq::launch_append_bf16(p, stream);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+        return ok();
+    }
     if (trace_on())
         fprintf(stderr, "[kvq] %s: B=%d H=%d T=%d D=%d R=%d bits=%d/%d blocks=%d\n", what, p.B, p.H, T, p.D, p.R,
                 p.k_bits, p.v_bits, n_cand);
@@ -360,6 +378,7 @@ enum class ChunkPath { kDecode, kCodes, kBand };
 
 ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
 {
+    if (c->k_bits == 16) return ChunkPath::kDecode;      // bf16 caches: the bf16 split kernel
     const bool big = chunk > 1 && c->head_dim >= 256;
     const int64_t rows = (int64_t)chunk * (n_q_heads / c->n_kv_heads);
     const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "codes" / "decode": force (measurement)
@@ -479,6 +498,7 @@ KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, in
 KVQ_API size_t kvq_decode_step_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_len)
 {
     if (check_cache(cache, "kvq_decode_step_workspace_bytes") != KVQ_OK) return SIZE_MAX;
+    if (cache->k_bits == 16) return SIZE_MAX;
     if (n_q_heads < 1 || n_q_heads % cache->n_kv_heads != 0 || max_len < 1) return SIZE_MAX;
     static const float dummy = 0.0f;
     ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, 1, &dummy, &dummy};
@@ -499,6 +519,8 @@ KVQ_API kvq_status kvq_decode_step(const kvq_cache* cache, const float* k, const
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1, k, v};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
+    if (cache->k_bits == 16)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: bf16 caches take kvq_append_quantize, then kvq_attn_decode", what);
     if (!k || !v) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k or v is NULL", what);
     if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k and v must be 16-byte aligned", what);

@@ -63,11 +63,15 @@ struct AttnParams {
     int32_t n_desc;
 };
 
+// Configuration id: 0..11 quantized (head_dim, k_bits, v_bits); 12..14 bf16
+// caches (head_dim 128, 256, 512).
 inline int cfg_id(int D, int kb, int vb)
 {
     const int di = D == 128 ? 0 : D == 256 ? 1 : 2;
+    if (kb == 16) return 12 + di;
     return di * 4 + (kb == 8 ? 2 : 0) + (vb == 8 ? 1 : 0);
 }
+inline bool cfg_is_bf16(int cfg) { return cfg >= 12; }
 
 // Partial buffer of one descriptor: o [B*Hkv*n_rt][S][16][D] fp32, then
 // (m, l) [B*Hkv*n_rt][S][16][2] fp32.
@@ -79,6 +83,8 @@ inline size_t part_floats(const AttnDesc& d)
 }
 
 hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
+hipError_t launch_append_bf16(const AppendParams& p, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);

@@ -66,6 +66,7 @@ typedef enum {
 
 #define KVQ_GROUP_SIZE 64          /* values per quantization group along head_dim      */
 #define KVQ_V_BLOCK 8              /* cache slots per V code block                      */
+#define KVQ_MIN_CAPACITY 32        /* smallest cache capacity (one 32-key read step)     */
 #define KVQ_MAX_SHARED_LAYERS 16   /* layers per kvq_shared_group                       */
 #define KVQ_MAX_SHARED_GROUPS 4    /* groups per kvq_attn_decode_shared call             */
 
@@ -87,8 +88,17 @@ typedef enum {
  * The blocked V layout puts the 8 codes of one head_dim element for 8
  * consecutive slots in one place, which is what the value contraction over
  * keys reads; keys are read along head_dim, so K stays token-major.
+ *
+ * Unquantized bf16 cache (k_bits == v_bits == 16): page 80, gemma4/model.ts,
+ * the note on cacheLayers, keeps the sliding layers' caches in bf16 under the
+ * model's other KV scheme.  The same layouts hold the bf16 bit patterns of the
+ * keys and values, rounded to nearest even from fp32, as 16-bit "codes" (K: 2
+ * per word; V: a block's 8 values of one element in 4 words); k_sb and v_sb are
+ * not used and may be NULL.  kvq_decode_step does not take such a cache.
+ *
  * Requirements: group_size == 64; head_dim in {128, 256, 512}; k_bits, v_bits in
- * {4, 8}; capacity a positive multiple of 8; 0 <= window <= capacity (0: full).
+ * {4, 8}, or both 16; capacity a multiple of 8 and at least KVQ_MIN_CAPACITY;
+ * 0 <= window <= capacity (0: full).
  */
 typedef struct {
     uint32_t *k_codes;
@@ -116,7 +126,8 @@ typedef struct {
  * last R tokens are written.  Slots that this call does not write keep their
  * contents (a V block shared with untouched slots is read, merged and written).
  * Inputs must be finite with |x| <= 1e38; outside that the written codes are
- * unspecified.
+ * unspecified.  A bf16 cache (k_bits == v_bits == 16) stores each value
+ * rounded to the nearest bf16, ties to even, at the same slots.
  */
 kvq_status kvq_append_quantize(const kvq_cache *cache,
                                const float *k, const float *v,

@@ -104,6 +104,11 @@ WORKLOADS: Dict[str, Workload] = {
             [QuerySpec("donor", 3, 8), QuerySpec("full", 1, 8, 5)],
             "mixed launch, B8: three layers decoding over a sliding cache (D256, K4/V8, window 512) "
             "and a 5-token verify chunk over a full layer (D512, K8/V8, 16384 tokens), one attention launch"),
+        _wl("sliding_decode_bf16_b8_w512", "decode",
+            [CacheSpec("kv", 8, 2, 256, 16, 16, 512, 512, 4096)],
+            [QuerySpec("kv", 1, 8)],
+            "sliding-window decode over an unquantized bf16 cache (the pages' bf16 sliding layers), B8, "
+            "8 q / 2 kv heads, D256, 4096 tokens through a ring of 512"),
         _wl("shared_decode_b32", "shared",
             [CacheSpec("donor", 32, 2, 256, 4, 4, 512, 512, 16384),
              CacheSpec("full", 32, 1, 512, 8, 8, 16384, 0, 16384)],

@@ -41,6 +41,15 @@ def assert_cache_equal(gpu_cache, ocache, batches=None):
     subset of GPU batch rows matching the oracle's batch axis)."""
     import oracle
     sel = slice(None) if batches is None else list(batches)
+    if ocache.k_vals is not None:           # bf16 cache: the values in the cache layouts
+        kv = ocache.k_vals.astype(np.uint32)
+        np.testing.assert_array_equal(u32(gpu_cache.k_codes)[sel], kv[..., 0::2] | (kv[..., 1::2] << 16),
+                                      err_msg="K bf16")
+        B, H, R, D = ocache.v_vals.shape
+        vb = ocache.v_vals.reshape(B, H, R // 8, 8, D).transpose(0, 1, 2, 4, 3).astype(np.uint32)
+        np.testing.assert_array_equal(u32(gpu_cache.v_codes)[sel], vb[..., 0::2] | (vb[..., 1::2] << 16),
+                                      err_msg="V bf16")
+        return
     k_words = u32(gpu_cache.k_codes)[sel]
     np.testing.assert_array_equal(k_words, oracle.pack_words(ocache.k_codes, ocache.k_bits), err_msg="K codes")
     np.testing.assert_array_equal(u32(gpu_cache.k_sb)[sel], sb_words(ocache.k_scales, ocache.k_biases),

@@ -49,7 +49,8 @@ def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAK
     (dict(head_dim=100), 2), (dict(head_dim=64), 2), (dict(group_size=32), 2), (dict(k_bits=5), 2),
     (dict(v_bits=2), 2), (dict(capacity=12), 1), (dict(capacity=0), 1), (dict(window=1024), 3),
     (dict(window=-1), 1), (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(k_codes=0), 1),
-    (dict(v_sb=0), 1),
+    (dict(v_sb=0), 1), (dict(capacity=24, window=0), 1), (dict(k_bits=16), 2), (dict(v_bits=16), 2),
+    (dict(k_bits=16, v_bits=16, v_codes=0), 1),
 ])
 def test_decode_cache_validation(lib, kw, status):
     assert decode(lib, cache(**kw)) == status
@@ -162,3 +163,18 @@ def test_decode_step_validation(lib):
     nb = lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 8, 600)
     assert nb not in (0, kvq.SIZE_MAX)
     assert lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 7, 600) == kvq.SIZE_MAX
+
+
+def test_bf16_cache_validation(lib):
+    """A bf16 cache (both widths 16) needs no scale/bias arrays; the fused decode
+    step does not take one.  Only host-side checks run here (no launch)."""
+    c = cache(k_bits=16, v_bits=16, k_sb=0, v_sb=0)
+    g, keep = _group(c, n_layers=3)
+    assert lib.kvq_decode_workspace_bytes(ctypes.byref(g), 1) != kvq.SIZE_MAX
+    assert lib.kvq_prefill_workspace_bytes(ctypes.byref(c), 8, 5, 4096) != kvq.SIZE_MAX
+    assert lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 8, 4096) == kvq.SIZE_MAX
+    st = lib.kvq_decode_step(ctypes.byref(c), FAKE, FAKE, FAKE, 8, FAKE, 4096, 1.0, FAKE, None, 0, None)
+    assert st == 2 and "bf16" in lib.kvq_last_error().decode()
+    mixed = cache(k_bits=16, v_bits=8, k_sb=0, v_sb=0)
+    g2, keep2 = _group(mixed)
+    assert lib.kvq_decode_workspace_bytes(ctypes.byref(g2), 1) == kvq.SIZE_MAX

@@ -35,7 +35,7 @@ def test_append_sequence_bitexact(D, kb, vb):
 
 def test_append_ring_offsets():
     """A T=1 append at every offset of a ring, then a wrap of T=R+5 from an odd start."""
-    B, H, D, R = 1, 1, 128, 24
+    B, H, D, R = 1, 1, 128, 40                    # not a multiple of the 32-key read step
     g = kvq.KVCache(B, H, D, 4, 8, R, window=R)
     o = oracle.Cache(B, H, D, R, 4, 8, window=R)
     for p in range(0, 2 * R + 3):
@@ -48,7 +48,7 @@ def test_append_ring_offsets():
 
 
 def test_append_adversarial_groups():
-    B, H, D, R = 1, 1, 128, 8
+    B, H, D, R = 1, 1, 128, 32
     vals = [
         np.full(64, 0.75, np.float32), np.full(64, -0.0, np.float32), np.full(64, 1e-30, np.float32),
         np.linspace(-1e30, 1e30, 64).astype(np.float32), np.array([-0.0] * 63 + [2.0 ** -20], np.float32),
@@ -66,7 +66,7 @@ def test_append_adversarial_groups():
 
 
 def test_append_denormal_inputs():
-    B, H, D, R = 1, 1, 128, 8
+    B, H, D, R = 1, 1, 128, 32
     k = (small_randn(7, (B, H, 8, D), 1.0) * 1e-39).astype(np.float32)   # fp32 subnormals
     g = kvq.KVCache(B, H, D, 4, 8, R)
     o = oracle.Cache(B, H, D, R, 4, 8)

@@ -105,7 +105,8 @@ def test_decode_split_invariance_and_determinism():
         assert_close(torch_bf16_to_f64(x), ref, "split")
 
 
-@pytest.mark.parametrize("name", ["decode_b1_l128", "sliding_decode_b8_w512", "full_decode_b4_l32768"])
+@pytest.mark.parametrize("name", ["decode_b1_l128", "sliding_decode_b8_w512", "full_decode_b4_l32768",
+                                  "sliding_decode_bf16_b8_w512"])
 def test_decode_workload(name):
     wl = WORKLOADS[name]
     print(f"workload {name}", flush=True)
