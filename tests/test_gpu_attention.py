@@ -388,3 +388,24 @@ def test_mixed_rejects_multi_layer_chunk():
     lens = torch.full((1,), 10, dtype=torch.int32, device="cuda")
     with pytest.raises(kvq.KvqError):
         kvq.kvq_attn_mixed([kvq.Read(g, [q, q], lens, 10)])
+
+
+@pytest.mark.parametrize("bits", [(4, 8), (8, 4), (16, 16)])
+def test_minimum_capacity_ring(bits):
+    """The smallest cache (32 slots) as a ring: every read step wraps inside it.
+    Decode at W = R and a chunk with W + C - 1 = R, against the oracle."""
+    kb, vb = bits
+    B, Hq, Hkv, D, R = 2, 8, 2, 256, 32
+    print(f"minimum capacity bits={bits}", flush=True)
+    g, o = make_pair(B, Hkv, D, kb, vb, R, R, 101, seed=17 + kb)
+    q = small_q_bits(18 + kb, (B, Hq, 1, D), D ** -0.25)
+    lens = np.full(B, 101, np.int32)
+    out = kvq.kvq_attn_decode(g, q_dev(q[:, :, 0].copy()), torch.from_numpy(lens).cuda(), 101)
+    torch.cuda.synchronize()
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens)[:, :, 0], f"decode R=32 bits={bits}")
+    g2, o2 = make_pair(B, Hkv, D, kb, vb, R, 16, 77, seed=19 + kb)
+    qc = small_q_bits(20 + kb, (B, Hq, 17, D), D ** -0.25)
+    lens2 = np.full(B, 77, np.int32)
+    out2 = kvq.kvq_attn_prefill_chunk(g2, q_dev(qc), torch.from_numpy(lens2).cuda(), 77)
+    torch.cuda.synchronize()
+    assert_close(torch_bf16_to_f64(out2), o2.attend(qc, lens2), f"chunk R=32 W=16 bits={bits}")
