@@ -353,11 +353,12 @@ def test_prefill_workload():
     print(f"prefill: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("with_d128", [False, True])
-def test_mixed_decode_and_verify_reads(with_d128):
+@pytest.mark.parametrize("extra", [None, "d128", "bf16"])
+def test_mixed_decode_and_verify_reads(extra):
     """Decode reads (several layers) and short chunks of other caches in one
-    kvq_attn_mixed call, ragged lengths; with a head_dim 128 read the call falls
-    back to one launch per read, without it all reads share one launch."""
+    kvq_attn_mixed call, ragged lengths; with a head_dim 128 read or a bf16 cache
+    the call falls back to one launch per read, without them all reads share one
+    launch."""
     B, L = 2, 900
     lens_np = np.array([L, L - 11], np.int32)
     lens = torch.from_numpy(lens_np).cuda()
@@ -366,15 +367,18 @@ def test_mixed_decode_and_verify_reads(with_d128):
         (1, 512, 8, 8, 1024, 0, 1, 8, 5),
         (2, 256, 8, 4, 136, 128, 1, 16, 8),
     ]
-    if with_d128:
+    if extra == "d128":
         specs.append((2, 128, 8, 4, 256, 200, 1, 4, 3))
+    if extra == "bf16":                                         # at most four reads per call
+        specs[2] = (2, 256, 16, 16, 520, 512, 1, 8, 5)        # a verify chunk on a bf16 ring
+        specs.append((1, 512, 16, 16, 1024, 0, 2, 8, 1))      # two layers decoding a bf16 full cache
     reads, refs = [], []
     for i, (Hkv, D, kb, vb, R, W, layers, Hq, C) in enumerate(specs):
         g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=400 + 10 * i)
         qs = [small_q_bits(500 + 10 * i + l, (B, Hq, C, D), D ** -0.25) for l in range(layers)]
         reads.append(kvq.Read(g, [q_dev(x) for x in qs], lens, L))
         refs.append([o.attend(x, lens_np) for x in qs])
-    print(f"mixed with_d128={with_d128}", flush=True)
+    print(f"mixed extra={extra}", flush=True)
     outs = kvq.kvq_attn_mixed(reads)
     torch.cuda.synchronize()
     for i in range(len(specs)):
