@@ -176,13 +176,12 @@ class Runner:
             spec = wl.caches[0]
             g = self.caches["kv"][0]
             nbytes = kvq.kvq_decode_workspace_bytes([(g, self.q["kv"], self.out["kv"], self.len["kv"], spec.length, 1.0)])
-            if spec.k_bits != 16:                 # the fused step takes quantized caches only
-                nbytes = max(nbytes, kvq.kvq_decode_step_workspace_bytes(g, wl.queries[0].Hq, spec.length))
+            nbytes = max(nbytes, kvq.kvq_decode_step_workspace_bytes(g, wl.queries[0].Hq, spec.length))
             k, v = self.step_kv["kv"]
             self.step_k1 = k.reshape(spec.B, spec.Hkv, spec.D)
             self.step_v1 = v.reshape(spec.B, spec.Hkv, spec.D)
         # decode steps run as one fused call (append + read); the others as two
-        self.fused = wl.kind == "decode" and wl.caches[0].k_bits != 16
+        self.fused = wl.kind == "decode"
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 

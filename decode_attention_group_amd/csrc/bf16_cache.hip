@@ -22,6 +22,15 @@
 // online softmax (base 2, lazy rescale) and accumulates O^T = V^T P^T for its
 // columns with the bf16 V block as the A operand and P in bf16 as B.  K and V
 // of the next step are loaded while the current one is computed.
+//
+// Fused decode step (page 80, attentionTraining: the token is appended, then
+// read): one more split per item takes the step's token at position len-1 --
+// the item of row tile 0 writes it into the cache, and every item emits, per
+// row, the partial m = scale*log2(e)*(q . k), l = 1, o = v of that one key
+// from the token's bf16-rounded values -- while the other splits leave that
+// position out.  The token's slot is outside every other split's range (and
+// outside the window of the position it replaces), so no read depends on the
+// write's timing.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -80,6 +89,69 @@ struct BfRegs {
 
 constexpr float kBfRescaleSlack = 8.0f;
 
+// The fused step's token split (see the header): 16 lanes per query row.
+template <int D>
+__device__ __forceinline__ void bf16_new_token(const AttnDesc& P, int bh, int rt, int s)
+{
+    constexpr int PARTS = 16, EPP = D / PARTS;     // elements per lane: 8, 16 or 32
+    const int tid = threadIdx.x;
+    const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
+    const int R = P.R, C = P.C;
+    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 1), P.max_len);
+    const int slot = (len - 1) % R;
+    const float* ksrc = as_global(P.k_new) + (int64_t)bh * D;
+    const float* vsrc = as_global(P.v_new) + (int64_t)bh * D;
+    if (rt == 0) {                                  // the cache write, once per (sequence, KV head)
+        // the cache arrays of a fused step are the caller's writable cache
+        uint32_t* kdst = const_cast<uint32_t*>(as_global(P.k_codes)) + ((int64_t)bh * R + slot) * (D / 2);
+        uint16_t* vdst = reinterpret_cast<uint16_t*>(const_cast<uint32_t*>(as_global(P.v_codes))) +
+                         (((int64_t)bh * (R / 8) + slot / 8) * D) * 8 + (slot & 7);
+        for (int d = 2 * tid; d < D; d += 2 * (int)blockDim.x) {
+            const float2 k2 = *reinterpret_cast<const float2*>(ksrc + d);
+            const float2 v2 = *reinterpret_cast<const float2*>(vsrc + d);
+            kdst[d / 2] = (uint32_t)f32_to_bf16_rne(k2.x) | ((uint32_t)f32_to_bf16_rne(k2.y) << 16);
+            vdst[(int64_t)d * 8] = f32_to_bf16_rne(v2.x);
+            vdst[(int64_t)(d + 1) * 8] = f32_to_bf16_rne(v2.y);
+        }
+    }
+    const int r = tid / PARTS, part = tid % PARTS;
+    const int grow = rt * kRowTile + r;
+    if (grow >= P.n_rows) return;
+    const int layer = C == 1 ? grow / P.hpk : 0;
+    const int qi = C == 1 ? 0 : grow / P.hpk;
+    const int hq = hkv * P.hpk + grow % P.hpk;
+    const uint16_t* qrow = as_global(P.q[layer]) + ((((int64_t)b * P.Hq + hq) * C + qi) * D) + part * EPP;
+    const float* kp = ksrc + part * EPP;
+    float acc = 0.0f;
+#pragma unroll
+    for (int e0 = 0; e0 < EPP; e0 += 8) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(qrow + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float k0 = __uint_as_float((uint32_t)f32_to_bf16_rne(kp[e0 + 2 * i]) << 16);
+            const float k1 = __uint_as_float((uint32_t)f32_to_bf16_rne(kp[e0 + 2 * i + 1]) << 16);
+            acc += bf16_lo_to_f32(u[i]) * k0 + bf16_hi_to_f32(u[i]) * k1;
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < PARTS; o <<= 1) acc += __shfl_xor(acc, o);
+    const int64_t prow = (((int64_t)bh * P.n_rt + rt) * P.S + s) * kRowTile + r;
+    float* po = as_global(P.part) + prow * D + part * EPP;
+    const float* vp = vsrc + part * EPP;
+#pragma unroll
+    for (int e0 = 0; e0 < EPP; e0 += 4) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __uint_as_float((uint32_t)f32_to_bf16_rne(vp[e0 + i]) << 16);
+        *reinterpret_cast<f32x4*>(po + e0) = o;
+    }
+    if (part == 0) {
+        float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * P.S * kRowTile * D + prow * 2;
+        pml[0] = acc * P.scale_log2e;
+        pml[1] = 1.0f;
+    }
+}
+
 __device__ __forceinline__ uint16_t bf16_bits_rne(float x) { return f32_to_bf16_rne(x); }
 
 template <int D>
@@ -99,6 +171,10 @@ __device__ __forceinline__ void attn_bf16_body(const AttnDesc& P, int idx, BfSme
     const int rt = (idx / S) % P.n_rt;
     const int bh = idx / (S * P.n_rt);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
+    if (P.k_new != nullptr && s == S - 1) {
+        bf16_new_token<D>(P, bh, rt, s);
+        return;
+    }
     const int R = P.R, W = P.W, C = P.C;
     const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
 
@@ -115,15 +191,15 @@ __device__ __forceinline__ void attn_bf16_body(const AttnDesc& P, int idx, BfSme
     const int hq = hkv * P.hpk + rsel % P.hpk;
     int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
     lo = max(lo, max(0, len - R));
-    const int hi = len - C + qi_hi;
+    const int hi = len - C + qi_hi - P.excl;        // excl: the fused step's token split has len-1
     const int base = lo & ~(kStep - 1);
     const int j0 = max(lo, base + s * P.split_len);
     const int j1 = min(hi + 1, base + (s + 1) * P.split_len);
     const int full_lo = max(j0, W > 0 ? len - C + qi_hi - W + 1 : 0);
-    const int full_hi = min(j1 - 1, len - C + qi_lo);
+    const int full_hi = min(j1 - 1, len - C + qi_lo - P.excl);
     const int p_row = len - C + qi;
     int klo = max(j0, W > 0 ? p_row - W + 1 : 0);
-    int khi = min(j1 - 1, p_row);
+    int khi = min(j1 - 1, p_row - P.excl);
     if (!row_ok) { klo = 1; khi = 0; }
     const int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
     const int st0 = j0 & ~(kStep - 1);

@@ -498,7 +498,6 @@ KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, in
 KVQ_API size_t kvq_decode_step_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_len)
 {
     if (check_cache(cache, "kvq_decode_step_workspace_bytes") != KVQ_OK) return SIZE_MAX;
-    if (cache->k_bits == 16) return SIZE_MAX;
     if (n_q_heads < 1 || n_q_heads % cache->n_kv_heads != 0 || max_len < 1) return SIZE_MAX;
     static const float dummy = 0.0f;
     ReadSpec r{cache, 1, nullptr, nullptr, n_q_heads, 1.0f, nullptr, max_len, 1, &dummy, &dummy};
@@ -519,8 +518,6 @@ KVQ_API kvq_status kvq_decode_step(const kvq_cache* cache, const float* k, const
     ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1, k, v};
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
-    if (cache->k_bits == 16)
-        return fail(KVQ_ERR_UNSUPPORTED, "%s: bf16 caches take kvq_append_quantize, then kvq_attn_decode", what);
     if (!k || !v) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k or v is NULL", what);
     if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k and v must be 16-byte aligned", what);

@@ -94,7 +94,8 @@ typedef enum {
  * model's other KV scheme.  The same layouts hold the bf16 bit patterns of the
  * keys and values, rounded to nearest even from fp32, as 16-bit "codes" (K: 2
  * per word; V: a block's 8 values of one element in 4 words); k_sb and v_sb are
- * not used and may be NULL.  kvq_decode_step does not take such a cache.
+ * not used and may be NULL.  Every call takes such a cache; kvq_decode_step
+ * rounds the step's token to bf16 where it would quantize it.
  *
  * Requirements: group_size == 64; head_dim in {128, 256, 512}; k_bits, v_bits in
  * {4, 8}, or both 16; capacity a multiple of 8 and at least KVQ_MIN_CAPACITY;

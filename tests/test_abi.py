@@ -166,15 +166,15 @@ def test_decode_step_validation(lib):
 
 
 def test_bf16_cache_validation(lib):
-    """A bf16 cache (both widths 16) needs no scale/bias arrays; the fused decode
-    step does not take one.  Only host-side checks run here (no launch)."""
+    """A bf16 cache (both widths 16) needs no scale/bias arrays and is taken by
+    every call.  Only host-side checks run here (no launch)."""
     c = cache(k_bits=16, v_bits=16, k_sb=0, v_sb=0)
     g, keep = _group(c, n_layers=3)
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(g), 1) != kvq.SIZE_MAX
     assert lib.kvq_prefill_workspace_bytes(ctypes.byref(c), 8, 5, 4096) != kvq.SIZE_MAX
-    assert lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 8, 4096) == kvq.SIZE_MAX
-    st = lib.kvq_decode_step(ctypes.byref(c), FAKE, FAKE, FAKE, 8, FAKE, 4096, 1.0, FAKE, None, 0, None)
-    assert st == 2 and "bf16" in lib.kvq_last_error().decode()
+    assert lib.kvq_decode_step_workspace_bytes(ctypes.byref(c), 8, 4096) != kvq.SIZE_MAX
+    st = lib.kvq_decode_step(ctypes.byref(c), FAKE + 4, FAKE, FAKE, 8, FAKE, 4096, 1.0, FAKE, None, 0, None)
+    assert st == 1 and "aligned" in lib.kvq_last_error().decode()     # refused before any launch
     mixed = cache(k_bits=16, v_bits=8, k_sb=0, v_sb=0)
     g2, keep2 = _group(mixed)
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(g2), 1) == kvq.SIZE_MAX

@@ -8,7 +8,8 @@ under the model's other KV scheme.  Checked here:
   * decode, chunk, KV-shared and mixed reads over bf16 caches are within the
     attention tolerance (max-abs 1e-2, mean-abs 1e-3) of the fp64 oracle, with
     ring wrap, ragged lengths, several row tiles and forced split counts;
-  * the fused decode step refuses a bf16 cache.
+  * the fused decode step writes the same cache words as the append and reads
+    within the same tolerance.
 """
 import os
 
@@ -159,11 +160,40 @@ def test_bf16_two_groups_one_launch():
     assert_close(torch_bf16_to_f64(res[1][0]), o2.attend(qb, full)[:, :, 0], "bf16 group 1")
 
 
-def test_bf16_decode_step_refused():
-    g = kvq.KVCache(1, 1, 128, 16, 16, 64)
-    k = torch.zeros(1, 1, 128, device="cuda")
-    q = torch.zeros(1, 8, 128, dtype=torch.bfloat16, device="cuda")
-    lens = torch.ones(1, dtype=torch.int32, device="cuda")
-    with pytest.raises(kvq.KvqError) as e:
-        kvq.kvq_decode_step(g, k, k, q, lens, 1)
-    assert e.value.status == 2
+STEP_CASES = [
+    # B, Hq, Hkv, D, R, W, history length
+    (2, 8, 2, 256, 512, 512, 1499),           # sliding ring wrap, the token replaces the oldest slot
+    (2, 8, 1, 512, 2048, 0, 1999),            # full layer, head_dim 512
+    (3, 4, 4, 128, 256, 100, 699),            # MHA, head_dim 128, window < R
+    (1, 40, 2, 256, 160, 0, 149),             # 20 rows: two row tiles
+    (1, 16, 1, 512, 64, 0, 0),                # the token is the only key
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bf16_decode_step(case):
+    """kvq_decode_step on a bf16 cache: the cache it leaves equals the one the
+    append writes for the same token, word for word, and the output is within
+    the attention tolerance of the oracle after its own append."""
+    B, Hq, Hkv, D, R, W, L = case
+    print(f"bf16 decode step {case}", flush=True)
+    if L > 0:
+        g, o = make_pair(B, Hkv, D, 16, 16, R, W, L, seed=sum(case) + 31)
+    else:
+        g, o = kvq.KVCache(B, Hkv, D, 16, 16, R, window=W), oracle.Cache(B, Hkv, D, R, 16, 16, window=W)
+    k = small_randn(sum(case) + 32, (B, Hkv, D), D ** -0.25)
+    v = small_randn(sum(case) + 33, (B, Hkv, D), D ** -0.25)
+    qb = small_q_bits(sum(case) + 34, (B, Hq, D), D ** -0.25)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    lens = np.full(B, L + 1, np.int32)
+    lens_d = torch.from_numpy(lens).cuda()
+    ref_cache = kvq.KVCache(B, Hkv, D, 16, 16, R, window=W)
+    ref_cache.k_codes.copy_(g.k_codes)
+    ref_cache.v_codes.copy_(g.v_codes)
+    kvq.kvq_append_quantize(ref_cache, kd[:, :, None].contiguous(), vd[:, :, None].contiguous(), lens_d - 1)
+    out = kvq.kvq_decode_step(g, kd, vd, q_dev(qb), lens_d, L + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(g.k_codes, ref_cache.k_codes) and torch.equal(g.v_codes, ref_cache.v_codes), "cache"
+    o.append(k[:, :, None], v[:, :, None], lens - 1)
+    assert_bf16_cache_equal(g, o, f"step {case}")
+    assert_close(torch_bf16_to_f64(out), o.attend(qb[:, :, None], lens)[:, :, 0], f"bf16 step {case}")
