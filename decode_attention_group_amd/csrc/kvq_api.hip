@@ -374,12 +374,19 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
 //     5 queries x 8 heads of B4 over 32768 keys of head_dim 512);
 //   band:   longer chunks: the chunk's key band is dequantized once into the
 //     workspace as bf16, then 32 query rows per workgroup (prefill.hip).
+// A bf16 cache takes the band path for chunks of more than 64 rows per KV head
+// (its band is a copy), else its own split kernel (bf16_cache.hip).
 enum class ChunkPath { kDecode, kCodes, kBand };
 
 ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
 {
-    if (c->k_bits == 16) return ChunkPath::kDecode;      // bf16 caches: the bf16 split kernel
     const bool big = chunk > 1 && c->head_dim >= 256;
+    if (c->k_bits == 16) {                 // bf16 caches: the bf16 split kernel, or the band (no short-chunk kernel)
+        const char* f = getenv("KVQ_PREFILL_PATH");
+        if (f && *f) return big && f[0] == 'b' ? ChunkPath::kBand : ChunkPath::kDecode;
+        return big && (int64_t)chunk * (n_q_heads / c->n_kv_heads) > kvq::kCodesPrefillRows ? ChunkPath::kBand
+                                                                                           : ChunkPath::kDecode;
+    }
     const int64_t rows = (int64_t)chunk * (n_q_heads / c->n_kv_heads);
     const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "codes" / "decode": force (measurement)
     if (e && *e) return !big ? ChunkPath::kDecode : e[0] == 'b' ? ChunkPath::kBand

@@ -180,6 +180,60 @@ __global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
 }
 
 // ---------------------------------------------------------------------------
+// Band of an unquantized bf16 cache (page 80, gemma4/model.ts, note on
+// cacheLayers: sliding layers stay bf16 under the other KV scheme): the same
+// tiles as band_dequant_kernel, copied from the stored bf16 values with no
+// arithmetic (a K row's words are already pairs in element order, a V block's
+// 16 bytes the 8 keys of one element).  Grid and thread mapping as above.
+template <int D>
+__global__ __launch_bounds__(256) void band_bf16_kernel(AttnDesc P)
+{
+    constexpr int KE = D / 8;                // K elements per thread
+    constexpr int VD = D / 256;              // elements d per thread (head_dim 256, 512)
+    const int tid = threadIdx.x;
+    const int step = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    const int bh = b * P.Hkv + hkv;
+    const int R = P.R;
+    const int len = min(max(__builtin_amdgcn_readfirstlane(as_global(P.len)[b]), 0), P.max_len);
+    const int vis_lo = band_lo(len, P.C, P.W, R);
+    const int p0 = (vis_lo & ~(kStep - 1)) + step * kStep;
+    if (p0 >= len) return;                   // past every query: never read
+    uint16_t* tile = as_global(P.band) + ((int64_t)bh * (P.nk / kStep + kBandPad) + step) * tile_elems<D>();
+    {   // K: key tid/8, elements [KE*(tid%8), +KE); positions no query sees are zeros
+        const int key = tid >> 3, ch = tid & 7;
+        const int kpos = p0 + key;
+        const bool kok = kpos >= vis_lo && kpos < len;
+        const uint32_t* src = as_global(P.k_codes) + ((int64_t)bh * R + kpos % R) * (D / 2) + ch * (KE / 2);
+        const int row = k_row(key);
+#pragma unroll
+        for (int e0 = 0; e0 < KE; e0 += 8) {
+            u32x4 x = *reinterpret_cast<const u32x4*>(src + e0 / 2);
+            if (!kok) x = (u32x4)0;
+            *reinterpret_cast<u32x4*>(tile + 8 * k_chunk_pos<D>(row, (ch * KE + e0) / 8)) = x;
+        }
+    }
+#pragma unroll
+    for (int dd = 0; dd < VD; ++dd) {       // V: element d, the step's 32 keys (4 blocks of 8 slots)
+        const int d = tid + 256 * dd;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int pos8 = p0 + 8 * blk;
+            const int slot8 = pos8 % R;                      // a multiple of 8
+            const u32x4 x = *reinterpret_cast<const u32x4*>(
+                as_global(P.v_codes) + (((int64_t)bh * (R / 8) + slot8 / 8) * D + d) * 4);
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool lo_ok = pos8 + 2 * i >= vis_lo && pos8 + 2 * i < len;
+                const bool hi_ok = pos8 + 2 * i + 1 >= vis_lo && pos8 + 2 * i + 1 < len;
+                w[i] = x[i] & ((lo_ok ? 0x0000FFFFu : 0u) | (hi_ok ? 0xFFFF0000u : 0u));
+            }
+            *reinterpret_cast<u32x4*>(tile + 8 * v_chunk_pos<D>(d, blk)) = (u32x4){w[0], w[1], w[2], w[3]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Attention over the dequantized band.
 //
 // A workgroup covers 32 query rows (two row tiles: the 8192 rows of a 512-query
@@ -525,6 +579,8 @@ hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stre
     KVQ_DQ(256, 4, 4) KVQ_DQ(256, 4, 8) KVQ_DQ(256, 8, 4) KVQ_DQ(256, 8, 8)
     KVQ_DQ(512, 4, 4) KVQ_DQ(512, 4, 8) KVQ_DQ(512, 8, 4) KVQ_DQ(512, 8, 8)
 #undef KVQ_DQ
+    case 13: band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d); break;   // bf16 caches
+    case 14: band_bf16_kernel<512><<<dq_grid, block, 0, stream>>>(d); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();

@@ -109,6 +109,11 @@ WORKLOADS: Dict[str, Workload] = {
             [QuerySpec("kv", 1, 8)],
             "sliding-window decode over an unquantized bf16 cache (the pages' bf16 sliding layers), B8, "
             "8 q / 2 kv heads, D256, 4096 tokens through a ring of 512"),
+        _wl("prefill_bf16_b2_c512_w512", "prefill",
+            [CacheSpec("kv", 2, 2, 256, 16, 16, 1024, 512, 8192 + 512)],
+            [QuerySpec("kv", 1, 8, 512)],
+            "chunked prefill over an unquantized bf16 cache (the pages' bf16 sliding layers), B2, 512-query "
+            "chunk after 8192 cached tokens, 8 q / 2 kv heads, D256, window 512 (ring of 1024)"),
         _wl("shared_decode_b32", "shared",
             [CacheSpec("donor", 32, 2, 256, 4, 4, 512, 512, 16384),
              CacheSpec("full", 32, 1, 512, 8, 8, 16384, 0, 16384)],

@@ -339,9 +339,10 @@ def test_prefill_split_invariance(splits):
     assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"prefill splits={splits}")
 
 
-def test_prefill_workload():
-    wl = WORKLOADS["prefill_b2_c512_w512"]
-    print("workload prefill_b2_c512_w512", flush=True)
+@pytest.mark.parametrize("name", ["prefill_b2_c512_w512", "prefill_bf16_b2_c512_w512"])
+def test_prefill_workload(name):
+    wl = WORKLOADS[name]
+    print(f"workload {name}", flush=True)
     gpu, orc, qd, _ = build_workload(wl)
     spec = wl.caches[0]
     q = qd[0][0]
@@ -349,8 +350,8 @@ def test_prefill_workload():
     out = kvq.kvq_attn_prefill_chunk(gpu["kv"], q_dev(q), torch.from_numpy(lens).cuda(), spec.length)
     torch.cuda.synchronize()
     o, _ = orc["kv"]
-    mx, mean = assert_close(torch_bf16_to_f64(out), o.attend(q, lens), "prefill workload")
-    print(f"prefill: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
+    mx, mean = assert_close(torch_bf16_to_f64(out), o.attend(q, lens), name)
+    print(f"{name}: max-abs {mx:.2e} mean-abs {mean:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("extra", [None, "d128", "bf16"])

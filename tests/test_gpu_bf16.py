@@ -100,23 +100,33 @@ def test_bf16_decode(case):
 
 CHUNK_CASES = [
     # B, Hq, Hkv, D, R, W, L, C
-    (2, 8, 2, 256, 520, 512, 1500, 5),        # verify window on a sliding ring
-    (2, 8, 2, 256, 1024, 512, 1200, 64),      # prefill chunk, window
+    (2, 8, 2, 256, 520, 512, 1500, 5),        # verify window on a sliding ring (split kernel)
+    (2, 8, 2, 256, 1024, 512, 1200, 64),      # prefill chunk, window (band: 256 rows per KV head)
     (1, 8, 1, 512, 4096, 0, 3000, 5),         # verify on a full layer
     (2, 4, 2, 128, 256, 0, 200, 17),          # head_dim 128, full
+    (1, 8, 1, 512, 2048, 0, 1500, 40),        # head_dim 512 band, full layer
+    (2, 8, 2, 256, 200, 64, 400, 96),         # band over a ring whose capacity is not a multiple of 32
 ]
 
 
+@pytest.mark.parametrize("path", ["auto", "band", "decode"])
 @pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_bf16_chunk(case):
+def test_bf16_chunk(case, path):
+    """Every case on the path the library picks and on each path forced (the
+    band exists for head_dim 256 and 512)."""
     B, Hq, Hkv, D, R, W, L, C = case
-    print(f"bf16 chunk {case}", flush=True)
+    print(f"bf16 chunk {case} path={path}", flush=True)
     g, o = make_pair(B, Hkv, D, 16, 16, R, W, L, seed=sum(case) + 9)
     q = small_q_bits(sum(case) + 10, (B, Hq, C, D), D ** -0.25)
     lens = np.full(B, L, np.int32)
-    out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
-    torch.cuda.synchronize()
-    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"bf16 chunk {case}")
+    if path != "auto":
+        os.environ["KVQ_PREFILL_PATH"] = path
+    try:
+        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("KVQ_PREFILL_PATH", None)
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"bf16 chunk {case} path={path}")
 
 
 def test_bf16_shared_with_quantized_group():
