@@ -58,7 +58,7 @@ extern "C" {
 typedef enum {
     KVQ_OK = 0,
     KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad count, Hq % Hkv != 0, ...      */
-    KVQ_ERR_UNSUPPORTED = 2,      /* bits not 4/8, group != 64, head_dim not 128/256/512 */
+    KVQ_ERR_UNSUPPORTED = 2,      /* bits not 4/8 (or both 16), group != 64, head_dim not 128/256/512 */
     KVQ_ERR_CAPACITY = 3,         /* window > capacity, cache cannot hold the visible keys */
     KVQ_ERR_WORKSPACE = 4,        /* workspace smaller than the *_workspace_bytes query  */
     KVQ_ERR_HIP = 5               /* a HIP launch error                                   */
