@@ -178,3 +178,23 @@ def test_bf16_cache_validation(lib):
     mixed = cache(k_bits=16, v_bits=8, k_sb=0, v_sb=0)
     g2, keep2 = _group(mixed)
     assert lib.kvq_decode_workspace_bytes(ctypes.byref(g2), 1) == kvq.SIZE_MAX
+
+
+@pytest.mark.parametrize("bits", [(4, 4), (4, 8), (8, 4), (8, 8), (16, 16)])
+def test_binding_buffers_follow_the_header_layouts(bits):
+    """KVCache allocates exactly the layouts include/kvq.h documents (host only:
+    the buffers live on the CPU here)."""
+    kb, vb = bits
+    B, H, D, R = 3, 2, 256, 96
+    c = kvq.KVCache(B, H, D, kb, vb, R, window=64, device="cpu")
+    assert tuple(c.k_codes.shape) == (B, H, R, D * kb // 32)
+    assert tuple(c.v_codes.shape) == (B, H, R // 8, D, vb // 4)
+    if kb == 16:
+        assert c.k_sb is None and c.v_sb is None
+        assert c.nbytes() == B * H * R * D * 2 * 2
+    else:
+        assert tuple(c.k_sb.shape) == (B, H, R, D // 64) == tuple(c.v_sb.shape)
+        assert c.nbytes() == B * H * R * (D * (kb + vb) // 8 + 2 * 4 * D // 64)
+    s = c.struct
+    assert (s.k_bits, s.v_bits, s.capacity, s.window, s.group_size) == (kb, vb, R, 64, 64)
+    assert (not s.k_sb) == (kb == 16)               # NULL (ctypes reads it back as None) for bf16
