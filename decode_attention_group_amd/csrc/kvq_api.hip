@@ -53,6 +53,13 @@ kvq_status check_cache(const kvq_cache* c, const char* what)
                     c->v_bits);
     if (c->batch < 1 || c->n_kv_heads < 1)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d and n_kv_heads %d must be >= 1", what, c->batch, c->n_kv_heads);
+    // launch grids put (2x) batch and the KV heads on 16-bit grid dimensions
+    if (c->batch > 32767 || c->n_kv_heads > 65535)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d or n_kv_heads %d too large", what, c->batch, c->n_kv_heads);
+    // rows and blocks are read with 16-byte loads
+    const uintptr_t ca = reinterpret_cast<uintptr_t>(c->k_codes) | reinterpret_cast<uintptr_t>(c->v_codes) |
+                         reinterpret_cast<uintptr_t>(c->k_sb) | reinterpret_cast<uintptr_t>(c->v_sb);
+    if (ca & 15) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: cache arrays must be 16-byte aligned", what);
     // a read loads the slots of a 32-key step as (step start mod R) + k, k < 32,
     // wrapped with one subtraction: in range for R >= 32
     if (c->capacity < KVQ_MIN_CAPACITY || c->capacity % KVQ_V_BLOCK != 0)
@@ -96,8 +103,12 @@ kvq_status check_read(const ReadSpec& r, const char* what)
     if (r.n_layers < 1 || r.n_layers > KVQ_MAX_SHARED_LAYERS)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_layers %d outside [1, %d]", what, r.n_layers, KVQ_MAX_SHARED_LAYERS);
     if (!r.q || !r.out) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q/out pointer array is NULL", what);
-    for (int l = 0; l < r.n_layers; ++l)
+    for (int l = 0; l < r.n_layers; ++l) {
         if (!r.q[l] || !r.out[l]) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q or out of layer %d is NULL", what, l);
+        // q rows are read with 16-byte loads, outputs written 8 bytes at a time
+        if ((reinterpret_cast<uintptr_t>(r.q[l]) & 15) || (reinterpret_cast<uintptr_t>(r.out[l]) & 7))
+            return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q of layer %d must be 16-byte and out 8-byte aligned", what, l);
+    }
     if (!r.len) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: len is NULL", what);
     if (r.Hq < 1 || r.Hq % c->n_kv_heads != 0)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_q_heads %d is not a positive multiple of n_kv_heads %d",

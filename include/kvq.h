@@ -43,6 +43,8 @@
  *     unspecified, though every memory access stays inside the cache.
  *   - Calls that share one cache, workspace or output on one device must be
  *     ordered (same stream or events); concurrent calls on such buffers race.
+ *   - Alignment: cache arrays, k and v 16 bytes; q 16 bytes; out 8 bytes
+ *     (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
  */
 #ifndef KVQ_H
 #define KVQ_H

@@ -50,7 +50,8 @@ def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAK
     (dict(v_bits=2), 2), (dict(capacity=12), 1), (dict(capacity=0), 1), (dict(window=1024), 3),
     (dict(window=-1), 1), (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(k_codes=0), 1),
     (dict(v_sb=0), 1), (dict(capacity=24, window=0), 1), (dict(k_bits=16), 2), (dict(v_bits=16), 2),
-    (dict(k_bits=16, v_bits=16, v_codes=0), 1),
+    (dict(k_bits=16, v_bits=16, v_codes=0), 1), (dict(k_codes=FAKE + 8), 1), (dict(v_sb=FAKE + 4), 1),
+    (dict(batch=40000), 1), (dict(n_kv_heads=70000), 1),
 ])
 def test_decode_cache_validation(lib, kw, status):
     assert decode(lib, cache(**kw)) == status
@@ -59,6 +60,9 @@ def test_decode_cache_validation(lib, kw, status):
 
 def test_decode_argument_validation(lib):
     assert decode(lib, cache(), Hq=7) == 1            # Hq % Hkv
+    assert decode(lib, cache(), q=FAKE + 2) == 1      # q not 16-byte aligned
+    assert decode(lib, cache(), out=FAKE + 4) == 1    # out not 8-byte aligned
+    assert "aligned" in lib.kvq_last_error().decode()
     assert decode(lib, cache(), q=0) == 1
     assert decode(lib, cache(), out=0) == 1
     assert decode(lib, cache(), ln=0) == 1
