@@ -202,3 +202,15 @@ def test_binding_buffers_follow_the_header_layouts(bits):
     s = c.struct
     assert (s.k_bits, s.v_bits, s.capacity, s.window, s.group_size) == (kb, vb, R, 64, 64)
     assert (not s.k_sb) == (kb == 16)               # NULL (ctypes reads it back as None) for bf16
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so,
+    before touching a GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
