@@ -46,16 +46,18 @@
  *   - Alignment: cache arrays, k and v 16 bytes; q 16 bytes; out 8 bytes
  *     (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
  *   - Precision: products accumulate in fp32 and out is rounded once to bf16.
- *     Decode reads, the decode step, shared and mixed reads, and chunks that
- *     take the split read multiply the codes exactly; q enters as fp16 (exact
- *     for 2^-14 <= |q| < 65504) and p * v_scale as fp16, so V scales must stay
- *     below 255.  Chunks of 17..64 query rows per KV head (rows = chunk * Hq/Hkv)
- *     with head_dim >= 256 over more than 2048 keys dequantize K and V to fp16
- *     (2^-11 relative; |value| < 65504).  Chunks of more than 64 rows per KV
- *     head with head_dim >= 256 dequantize K and V to bf16 tiles (2^-9
- *     relative), which moves a logit by up to scale * 2^-9 * sum_i |q_i k_i|:
- *     negligible at scale 1.0 on RMS-normalised q and k, a few hundredths of
- *     an output when the logits spread over hundreds.
+ *     On quantized caches, decode reads, the decode step, shared and mixed
+ *     reads, and chunks that take the split read multiply the codes exactly; q
+ *     enters as fp16 (exact for 2^-14 <= |q| < 65504) and p * v_scale as fp16,
+ *     so V scales must stay below 255.  Chunks of 17..64 query rows per KV head
+ *     (rows = chunk * Hq/Hkv) with head_dim >= 256 over more than 2048 keys
+ *     dequantize K and V to fp16 (2^-11 relative; |value| < 65504); chunks of
+ *     more than 64 rows per KV head with head_dim >= 256 dequantize them to
+ *     bf16 tiles (2^-9 relative), which moves a logit by up to
+ *     scale * 2^-9 * sum_i |q_i k_i|: negligible at scale 1.0 on RMS-normalised
+ *     q and k, a few hundredths of an output when the logits spread over
+ *     hundreds.  Reads of bf16 caches multiply the stored values exactly, with
+ *     q as bf16 and the softmax weights rounded to bf16 for the value product.
  */
 #ifndef KVQ_H
 #define KVQ_H
