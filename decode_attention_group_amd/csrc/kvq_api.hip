@@ -416,6 +416,18 @@ int64_t band_positions(const kvq_cache* c, int chunk, int max_len)
     return (span + 2 * kvq::kStep - 1) / kvq::kStep * kvq::kStep;
 }
 
+// A bf16 cache's chunk is read by the attention kernel straight from the cache
+// (no band copy) when every byte offset inside one (sequence, KV head) fits the
+// kernel's unsigned 32-bit DMA offsets; KVQ_BF16_BAND=1 forces the band copy
+// (measurement).
+bool band_direct(int cfg, int R, int D)
+{
+    if (!kvq::cfg_is_bf16(cfg)) return false;
+    const char* e = getenv("KVQ_BF16_BAND");
+    if (e && e[0] == '1') return false;
+    return (int64_t)R * D * 2 < ((int64_t)1 << 31);
+}
+
 size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
 {
     std::memset(&P, 0, sizeof(P));
@@ -445,6 +457,7 @@ size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
     // workspace: split partials, then the band tiles (K and V, bf16; four spare
     // tiles per sequence and KV head that a final prefetch may read)
     const size_t part = (kvq::part_floats(d) * sizeof(float) + 255) & ~(size_t)255;
+    if (band_direct(d.cfg, d.R, d.D)) return part;
     return part + (size_t)d.B * d.Hkv * (d.nk + 4 * kvq::kStep) * d.D * 2 * sizeof(uint16_t);
 }
 
@@ -483,7 +496,7 @@ void bind_prefill_workspace(kvq::AttnParams& P, void* workspace)
     char* base = static_cast<char*>(workspace);
     const size_t part = (kvq::part_floats(d) * sizeof(float) + 255) & ~(size_t)255;
     d.part = kvq::part_floats(d) ? reinterpret_cast<float*>(base) : nullptr;
-    d.band = reinterpret_cast<uint16_t*>(base + part);
+    d.band = band_direct(d.cfg, d.R, d.D) ? nullptr : reinterpret_cast<uint16_t*>(base + part);
 }
 
 KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t chunk, int32_t max_len)

@@ -44,7 +44,8 @@ struct AttnDesc {
     int32_t excl;           // 1: the attention splits leave out position len-1 (fused step)
     float* part;            // split partials (null when S == 1)
     uint16_t* band;         // prefill: dequantized band tiles, bf16 [B][Hkv][nk/32][64*D] (the
-                            // LDS image of each 32-key step: K rows, then V^T rows, swizzled)
+                            // LDS image of each 32-key step: K rows, then V^T rows, swizzled);
+                            // null for a bf16 cache that the attention kernel reads in place
     int32_t nk;             // prefill: band positions held per (b, kv head), a multiple of 32
     int32_t B, Hkv, Hq, R, W, C, D;
     int32_t max_len;        // len[b] is clamped to [0, max_len]

@@ -25,6 +25,12 @@
 //     alternate steps and merge in LDS at the end.  S^T = K Q^T and
 //     O^T = V^T P^T run on 16x16x32 bf16 MFMA with an online softmax in base 2
 //     (lazy rescale: the running max may trail the true one by up to 2^8).
+// An unquantized bf16 cache needs no dequantization: the attention kernel then
+// DMAs each step's tiles straight from the cache (every lane addressing its own
+// 16-byte chunk, the same LDS image), and zeroes the V^T entries of positions
+// outside the band, which a ring slot or a never-written slot may fill with
+// anything.  band_bf16_kernel (the band as a copy) remains for caches too large
+// for 32-bit DMA offsets.
 // Rows follow the decode layout (row = query * (Hq/Hkv) + head), so split
 // partials, if any, go through the same combine kernel.
 #include <type_traits>
@@ -282,7 +288,64 @@ __device__ __forceinline__ void dma_round(PfSmem<D>& sm, int slot, const uint16_
     }
 }
 
+// The same round copied straight from a bf16 cache (no band): every lane
+// addresses its own 16-byte chunk.  Tile chunk ci of step g (position pos_g, a
+// multiple of 32) is, in the K part, chunk c = (ci mod D/8) ^ (row mod 16) of
+// the key that LDS row ci / (D/8) holds (k_row inverted), and in the V part the
+// 8 keys 8c .. 8c+7 of element d, c = (ci mod 4) ^ ((d / 4) mod 4): one cache V
+// block entry.  Slots wrap modulo R (R >= 32 and a multiple of 8, so a step
+// base plus 31 wraps at most once and a V block never straddles the wrap).
+// Offsets are unsigned 32-bit from the (sequence, KV head) base, which the host
+// guarantees by R * D * 2 < 2^31.
 template <int D>
+__device__ __forceinline__ void dma_round_direct(PfSmem<D>& sm, int slot, uint64_t kbase, uint64_t vbase,
+                                                 int pos0, int R, int tid)
+{
+    constexpr int NT = 64 * pf_waves<D>();
+    constexpr int NG = pf_groups<D>();
+    constexpr int JT = 8 * D / NT;                   // instructions per step tile
+    constexpr int JK = 4 * D / NT;                   // of which K
+    static_assert(JT * NT == 8 * D && JK * NT == 4 * D, "whole chunks per thread");
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(&sm.tile[slot][0][0]) + (tid & ~63) * 16);
+    int pm[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) pm[g] = __builtin_amdgcn_readfirstlane((pos0 + g * kStep) % R);
+#pragma unroll
+    for (int j = 0; j < NG * JT; ++j) {
+        const int g = j / JT, jj = j % JT;
+        uint32_t off;
+        uint64_t base;
+        if (jj < JK) {
+            const int ci = jj * NT + tid;
+            const int row = ci / (D / 8), r16 = row & 15;
+            const int c = (ci % (D / 8)) ^ r16;
+            const int key = 8 * (r16 >> 2) + 4 * (row >> 4) + (r16 & 3);
+            int sl = pm[g] + key;
+            sl = sl >= R ? sl - R : sl;
+            off = (uint32_t)sl * (uint32_t)(D * 2) + (uint32_t)c * 16u;
+            base = kbase;
+        } else {
+            const int cv = (jj - JK) * NT + tid;
+            const int d = cv >> 2;
+            const int c = (cv & 3) ^ ((d >> 2) & 3);
+            int s8 = pm[g] + 8 * c;
+            s8 = s8 >= R ? s8 - R : s8;
+            off = ((uint32_t)(s8 >> 3) * (uint32_t)D + (uint32_t)d) * 16u;
+            base = vbase;
+        }
+        uint32_t saved;
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %1\n\t"
+                     "s_nop 0\n\t"
+                     "global_load_lds_dwordx4 %2, %3\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "s"(lds0 + j * NT * 16), "v"(off), "s"(base)
+                     : "memory");
+    }
+}
+
+template <int D, bool DIRECT>
 __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<D>& sm)
 {
     constexpr int NG = pf_groups<D>(), RT = pf_rt<D>();
@@ -344,10 +407,12 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
     // ---- key ranges for a given len: the block's keys [j0, j1) in nsteps steps
     //      from st0, each row's [klo, khi], the keys every row of the wave sees
     //      [full_lo, full_hi], and the band tile t0 of step st0
-    int j0, j1, nsteps, st0, full_lo, full_hi, t0;
+    int j0, j1, nsteps, st0, full_lo, full_hi, t0, vis_lo, len_p;
     int klo[RT], khi[RT];
     auto plan = [&](int len) {
-        const int base0 = band_lo(len, C, W, R) & ~(kStep - 1);
+        vis_lo = band_lo(len, C, W, R);
+        len_p = len;
+        const int base0 = vis_lo & ~(kStep - 1);
         int lo = W > 0 ? len - C + qi_lo - W + 1 : 0;
         lo = max(lo, max(0, len - R));
         const int hi = len - C + qi_hi;
@@ -368,10 +433,14 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
         t0 = (st0 - base0) / kStep;
     };
 
-    // ---- step tiles of the band: round u copies band tiles t0 + NG*u .. +NG-1
-    const uint16_t* band_bh = as_global(P.band) + (int64_t)bh * (P.nk / kStep + kBandPad) * tile_elems<D>();
+    // ---- step tiles: round u copies band tiles t0 + NG*u .. +NG-1, or (DIRECT,
+    //      a bf16 cache) the same steps st0 + kStep*(NG*u + g) from the cache
+    const uint16_t* band_bh = DIRECT ? nullptr : as_global(P.band) + (int64_t)bh * (P.nk / kStep + kBandPad) * tile_elems<D>();
+    const uint64_t kbase = (uint64_t)(uintptr_t)(P.k_codes + (int64_t)bh * R * (D / 2));
+    const uint64_t vbase = (uint64_t)(uintptr_t)(P.v_codes + (int64_t)bh * (R / 8) * D * 4);
     auto copy_round = [&](int u, int slot) {
-        dma_round<D>(sm, slot, band_bh + (int64_t)(t0 + NG * u) * tile_elems<D>(), tid);
+        if constexpr (DIRECT) dma_round_direct<D>(sm, slot, kbase, vbase, st0 + NG * u * kStep, R, tid);
+        else dma_round<D>(sm, slot, band_bh + (int64_t)(t0 + NG * u) * tile_elems<D>(), tid);
     };
     plan(P.max_len);
     copy_round(0, 0);
@@ -422,6 +491,19 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
                     }
                 }
         }
+        // DIRECT: slots of positions outside [vis_lo, len) may hold anything
+        // (a stale ring entry, a never-written slot); their weights are 0, and
+        // their V^T entries are zeroed here so 0 * NaN cannot reach O.  Keys
+        // 8*lg .. 8*lg+7 of the step are this lane's V^T columns.
+        u32x4 vmask = (u32x4){~0u, ~0u, ~0u, ~0u};
+        if constexpr (DIRECT && !FULL) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k0 = st + 8 * lg + 2 * i;
+                vmask[i] = (k0 >= vis_lo && k0 < len_p ? 0x0000FFFFu : 0u) |
+                           (k0 + 1 >= vis_lo && k0 + 1 < len_p ? 0xFFFF0000u : 0u);
+            }
+        }
         bf16x8 pb[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -451,7 +533,8 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.tile[slot][grp][8 * v_chunk_pos<D>(16 * dt + m, lg)]);
+            bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.tile[slot][grp][8 * v_chunk_pos<D>(16 * dt + m, lg)]);
+            if constexpr (DIRECT && !FULL) a = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, a) & vmask);
 #pragma unroll
             for (int r = 0; r < RT; ++r) O[r][dt] = mfma_bf16(a, pb[r], O[r][dt]);
         }
@@ -561,11 +644,11 @@ __device__ __forceinline__ int xcd_item(int bid, int n)
     return x * q + min(x, r) + k;
 }
 
-template <int D>
+template <int D, bool DIRECT>
 __global__ __launch_bounds__(64 * pf_waves<D>()) void prefill_kernel(AttnParams P)
 {
     __shared__ PfSmem<D> sm;
-    prefill_body<D>(P.d[0], xcd_item(blockIdx.x, gridDim.x), sm);
+    prefill_body<D, DIRECT>(P.d[0], xcd_item(blockIdx.x, gridDim.x), sm);
 }
 
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream)
@@ -579,15 +662,27 @@ hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stre
     KVQ_DQ(256, 4, 4) KVQ_DQ(256, 4, 8) KVQ_DQ(256, 8, 4) KVQ_DQ(256, 8, 8)
     KVQ_DQ(512, 4, 4) KVQ_DQ(512, 4, 8) KVQ_DQ(512, 8, 4) KVQ_DQ(512, 8, 8)
 #undef KVQ_DQ
-    case 13: band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d); break;   // bf16 caches
-    case 14: band_bf16_kernel<512><<<dq_grid, block, 0, stream>>>(d); break;
+    case 13: case 14:      // bf16 caches: the attention kernel reads the cache itself (no band)
+        if (d.band != nullptr) {
+            if (d.cfg == 13) band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d);
+            else band_bf16_kernel<512><<<dq_grid, block, 0, stream>>>(d);
+        }
+        break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d.D == 256) prefill_kernel<256><<<dim3(total_items), dim3(64 * pf_waves<256>()), 0, stream>>>(p);
-    else if (d.D == 512) prefill_kernel<512><<<dim3(total_items), dim3(64 * pf_waves<512>()), 0, stream>>>(p);
-    else return hipErrorInvalidValue;
+    const bool direct = cfg_is_bf16(d.cfg) && d.band == nullptr;
+    const dim3 grid(total_items);
+    if (d.D == 256) {
+        if (direct) prefill_kernel<256, true><<<grid, dim3(64 * pf_waves<256>()), 0, stream>>>(p);
+        else prefill_kernel<256, false><<<grid, dim3(64 * pf_waves<256>()), 0, stream>>>(p);
+    } else if (d.D == 512) {
+        if (direct) prefill_kernel<512, true><<<grid, dim3(64 * pf_waves<512>()), 0, stream>>>(p);
+        else prefill_kernel<512, false><<<grid, dim3(64 * pf_waves<512>()), 0, stream>>>(p);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -109,24 +109,62 @@ CHUNK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("path", ["auto", "band", "decode"])
+PATH_ENV = {
+    "auto": {},
+    "band": {"KVQ_PREFILL_PATH": "band"},                          # attention reads the cache in place
+    "band_copy": {"KVQ_PREFILL_PATH": "band", "KVQ_BF16_BAND": "1"},   # band copy kernel first
+    "decode": {"KVQ_PREFILL_PATH": "decode"},
+}
+
+
+def chunk_read(g, q, lens, L, path):
+    env = PATH_ENV[path]
+    os.environ.update(env)
+    try:
+        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+        torch.cuda.synchronize()
+    finally:
+        for k in env:
+            os.environ.pop(k, None)
+    return out
+
+
+@pytest.mark.parametrize("path", list(PATH_ENV))
 @pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_bf16_chunk(case, path):
     """Every case on the path the library picks and on each path forced (the
-    band exists for head_dim 256 and 512)."""
+    band exists for head_dim 256 and 512; on a bf16 cache the attention kernel
+    reads the cache in place unless the band copy is forced)."""
     B, Hq, Hkv, D, R, W, L, C = case
     print(f"bf16 chunk {case} path={path}", flush=True)
     g, o = make_pair(B, Hkv, D, 16, 16, R, W, L, seed=sum(case) + 9)
     q = small_q_bits(sum(case) + 10, (B, Hq, C, D), D ** -0.25)
     lens = np.full(B, L, np.int32)
-    if path != "auto":
-        os.environ["KVQ_PREFILL_PATH"] = path
-    try:
-        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
-        torch.cuda.synchronize()
-    finally:
-        os.environ.pop("KVQ_PREFILL_PATH", None)
+    out = chunk_read(g, q, lens, L, path)
     assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"bf16 chunk {case} path={path}")
+
+
+@pytest.mark.parametrize("path", ["band", "band_copy", "decode"])
+@pytest.mark.parametrize("W", [0, 256])
+def test_bf16_chunk_unwritten_slots_hold_nan(path, W):
+    """Slots that no append wrote hold NaN bit patterns (the library does not
+    ask for zeroed caches).  The reads fetch whole 32-key steps, so the last
+    step reaches slots past len; those keys get weight 0 and their values must
+    not reach the output."""
+    B, Hq, Hkv, D, R, L, C = 2, 8, 2, 256, 1024, 333, 80
+    g = kvq.KVCache(B, Hkv, D, 16, 16, R, window=W)
+    g.k_codes.fill_(-1)                       # 0xFFFF halves: bf16 NaN
+    g.v_codes.fill_(-1)
+    o = oracle.Cache(B, Hkv, D, R, 16, 16, window=W)
+    k = small_randn(31, (B, Hkv, L, D), D ** -0.25)
+    v = small_randn(32, (B, Hkv, L, D), D ** -0.25)
+    pos0 = np.zeros(B, np.int32)
+    kvq.kvq_append_quantize(g, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), torch.from_numpy(pos0).cuda())
+    o.append(k, v, pos0)
+    q = small_q_bits(33, (B, Hq, C, D), D ** -0.25)
+    lens = np.full(B, L, np.int32)
+    out = chunk_read(g, q, lens, L, path)
+    assert_close(torch_bf16_to_f64(out), o.attend(q, lens), f"bf16 chunk over NaN slots W={W} path={path}")
 
 
 def test_bf16_shared_with_quantized_group():
