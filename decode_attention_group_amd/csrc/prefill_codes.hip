@@ -180,9 +180,15 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
         w[0] = as_global(P.k_sb)[kslot0 * G + o];
         w[1] = as_global(P.v_sb)[kslot0 * G + o];
     };
-    auto stage_sb = [&](const uint32_t (&w)[2], int slot) {
+    // Positions at or past len (the tail of the last step) may sit in slots no
+    // append wrote, whose words can be anything (NaN included); their scale and
+    // bias are staged as 0, so they dequantize to 0 and a zero weight cannot
+    // meet a NaN value.
+    auto stage_sb = [&](const uint32_t (&w_in)[2], int slot, int st) {
         if (NSB >= NT || tid < NSB) {
             const int g = sb_g % G, key = sb_key;
+            const bool held = st + key < len;
+            const uint32_t w[2] = {held ? w_in[0] : 0u, held ? w_in[1] : 0u};
             // V scale/bias go to the V^T element position of the key
             const int j = key & 7;
             const int pos = (key & ~7) + (VB == 8 ? j : (j < 4 ? 2 * j : 2 * (j - 4) + 1));
@@ -348,8 +354,8 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
             load_codes(cs[r], stp(r));
             load_sb(sbs[(r + 1) % NSET], stp(r + 1));
         });
-        stage_sb(s0, 0);
-        stage_sb(sbs[1], 1);
+        stage_sb(s0, 0, stp(0));
+        stage_sb(sbs[1], 1, stp(1));
         __syncthreads();
         dequant(cs[0], 0);
         __syncthreads();
@@ -362,7 +368,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
             const int slot = h & 1;
             load_codes(cs[r], stp(h + NSET));
             load_sb(sbs[(r + 1) % NSET], stp(h + NSET + 1));
-            stage_sb(sbs[(r + 2) % NSET], slot);
+            stage_sb(sbs[(r + 2) % NSET], slot, stp(h + 2));
             if (h + 1 < nsteps) dequant(cs[(r + 1) % NSET], slot ^ 1);
             do_compute(st0 + h * kStep, slot);
             __syncthreads();

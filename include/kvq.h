@@ -100,6 +100,10 @@ typedef enum {
  *   k_sb, v_sb  uint32 [B][H][R][G]  per slot and group: bf16 scale in bits 0..15,
  *            bf16 bias in bits 16..31
  *
+ * A cache needs no clearing before its first append: reads fetch whole 32-key
+ * steps and so touch slots past len that no append wrote, but such slots get
+ * weight 0 and their contents (NaN bit patterns included) never reach out.
+ *
  * The blocked V layout puts the 8 codes of one head_dim element for 8
  * consecutive slots in one place, which is what the value contraction over
  * keys reads; keys are read along head_dim, so K stays token-major.
