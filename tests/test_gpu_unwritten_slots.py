@@ -7,7 +7,8 @@ whatever the memory held.  Here those words are all-ones: bf16 NaN scales and
 biases, and maximal codes.  Such keys get weight 0 and must not reach the
 output on any path: the split read, the fused decode step, the short-chunk
 kernel (more than 16 and at most 64 rows per KV head over more than 2048 keys)
-and the band path.  Outputs within the attention tolerance of the oracle."""
+and the band path; on a bf16 cache the unwritten values themselves are NaN.
+Outputs within the attention tolerance of the oracle."""
 import os
 
 import numpy as np
@@ -26,7 +27,8 @@ pytestmark = pytest.mark.gpu
 def garbage_pair(B, H, D, kb, vb, R, W, L, seed):
     g = kvq.KVCache(B, H, D, kb, vb, R, window=W, zero=False)
     for t in (g.k_codes, g.v_codes, g.k_sb, g.v_sb):
-        t.fill_(-1)
+        if t is not None:                     # bf16 caches have no scale/bias arrays
+            t.fill_(-1)
     o = oracle.Cache(B, H, D, R, kb, vb, window=W)
     k = small_randn(seed, (B, H, L, D), D ** -0.25)
     v = small_randn(seed + 1, (B, H, L, D), D ** -0.25)
@@ -36,11 +38,11 @@ def garbage_pair(B, H, D, kb, vb, R, W, L, seed):
     return g, o
 
 
-def chunk(g, q, lens, L, path):
+def chunk(g, q, lens, max_len, path):
     if path != "auto":
         os.environ["KVQ_PREFILL_PATH"] = path
     try:
-        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), L)
+        out = kvq.kvq_attn_prefill_chunk(g, q_dev(q), torch.from_numpy(lens).cuda(), max_len)
         torch.cuda.synchronize()
     finally:
         os.environ.pop("KVQ_PREFILL_PATH", None)
@@ -52,24 +54,29 @@ CASES = [
     (1, 8, 1, 512, 8, 8, 4096, 0, 3000),      # full layer: 5-query chunks take the short-chunk kernel
     (2, 8, 2, 256, 4, 8, 1024, 512, 700),     # sliding ring, not yet wrapped
     (2, 8, 2, 256, 4, 4, 4096, 0, 2500),      # full layer, head_dim 256
+    (2, 8, 2, 256, 16, 16, 1024, 0, 700),     # bf16 cache, full layer (NaN values past len)
 ]
 
 
+@pytest.mark.parametrize("slack", [0, 300])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
-def test_reads_ignore_unwritten_slots(case):
+def test_reads_ignore_unwritten_slots(case, slack):
+    """max_len = len + slack: with slack the launches are sized past every
+    sequence's length, so more steps reach unwritten slots."""
     B, Hq, Hkv, D, kb, vb, R, W, L = case
-    print(f"unwritten slots {case}", flush=True)
+    M = L + slack
+    print(f"unwritten slots {case} max_len={M}", flush=True)
     g, o = garbage_pair(B, Hkv, D, kb, vb, R, W, L, seed=sum(case))
     lens = np.full(B, L, np.int32)
     qd = small_q_bits(sum(case) + 2, (B, Hq, 1, D), D ** -0.25)
-    out = kvq.kvq_attn_decode(g, q_dev(qd[:, :, 0].copy()), torch.from_numpy(lens).cuda(), L)
+    out = kvq.kvq_attn_decode(g, q_dev(qd[:, :, 0].copy()), torch.from_numpy(lens).cuda(), M)
     torch.cuda.synchronize()
     assert_close(torch_bf16_to_f64(out), o.attend(qd, lens)[:, :, 0], f"decode {case}")
     for C, paths in ((5, ("auto", "codes", "band", "decode")), (100, ("auto", "band", "decode"))):
         qc = small_q_bits(sum(case) + 3 + C, (B, Hq, C, D), D ** -0.25)
         ref = o.attend(qc, lens)
         for path in paths:
-            out = chunk(g, qc, lens, L, path)
+            out = chunk(g, qc, lens, M, path)
             assert_close(torch_bf16_to_f64(out), ref, f"chunk C={C} path={path} {case}")
 
 
