@@ -27,6 +27,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
+# An AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, loaded
+# instead when KVQO_SANITIZE=1 (the process must preload the sanitizer runtime).
+_LIB_SAN = os.path.join(_HERE, "libkvq_oracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 GROUP = 64
 
 _lib = None
@@ -40,25 +44,31 @@ class OracleError(RuntimeError):
         self.status = status
 
 
-def build(force: bool = True) -> str:
-    """Compile kvq_oracle.c with gcc (IEEE fp32, no contraction, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+def _sanitized() -> bool:
+    return os.environ.get("KVQO_SANITIZE") == "1"
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile kvq_oracle.c with gcc (IEEE fp32, no contraction, OpenMP); with
+    sanitize=True the AddressSanitizer/UBSan build beside it."""
+    lib = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp"
         subprocess.check_call([
             "gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
             "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+            *(_SAN_FLAGS if sanitize else []),
             _SRC, "-o", tmp, "-lm",
         ])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        path = build(force=False, sanitize=_sanitized())
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32 = ctypes.c_int
         lib.kvqo_quantize_group.argtypes = [P, i32, i32, P, P, P]

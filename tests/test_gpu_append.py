@@ -86,3 +86,47 @@ def test_append_workload_caches(name):
     for cname, g in gpu.items():
         o, sel = orc[cname]
         assert_cache_equal(g, o, batches=sel if len(sel) != g.batch else None)
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 8), (8, 4)])
+def test_append_exact_ties(kb, vb):
+    """Groups whose code ratios land exactly on k + 1/2 (and one fp32 step off):
+    codes round half to even, bit-exact with the oracle."""
+    import quant_reference as qref
+    B, H, D, R = 1, 2, 256, 64
+    per = D // 64
+    Xk, _ = qref.tie_groups(np.random.default_rng(40 + kb), kb, B * H * R * per)
+    Xv, _ = qref.tie_groups(np.random.default_rng(50 + vb), vb, B * H * R * per)
+    k = np.ascontiguousarray(Xk.reshape(B, H, R, D))
+    v = np.ascontiguousarray(Xv.reshape(B, H, R, D))
+    g = kvq.KVCache(B, H, D, kb, vb, R)
+    o = oracle.Cache(B, H, D, R, kb, vb)
+    _append_both(g, o, k, v, [0])
+    torch.cuda.synchronize()
+    assert_cache_equal(g, o)
+
+
+def test_append_golden_groups():
+    """The hand-worked groups (exact ties included) through the GPU append: K at
+    4 bits holds the 4-bit examples, V at 8 bits the 8-bit ones, each group at
+    every position of a 128-wide row, so every lane position meets every example."""
+    from test_oracle_quant import _golden_rows
+    rows = _golden_rows()
+    g4 = [r[2] for r in rows if r[1] == 4]
+    g8 = [r[2] for r in rows if r[1] == 8]
+    B, H, D, R = 1, 1, 128, 32
+    T = max(len(g4), len(g8)) * 2
+    k = np.zeros((B, H, T, D), np.float32)
+    v = np.zeros((B, H, T, D), np.float32)
+    for t in range(T):
+        for grp in range(2):
+            k[0, 0, t, grp * 64:(grp + 1) * 64] = g4[(t + grp) % len(g4)]
+            v[0, 0, t, grp * 64:(grp + 1) * 64] = g8[(t + grp) % len(g8)]
+    g = kvq.KVCache(B, H, D, 4, 8, R)
+    o = oracle.Cache(B, H, D, R, 4, 8)
+    _append_both(g, o, k, v, [0])
+    torch.cuda.synchronize()
+    assert_cache_equal(g, o)
+    for name, bits, x, codes, s, b in rows:       # and the oracle holds the hand values
+        c, sb, bb = oracle.quantize_group(x, bits)
+        assert (c == codes).all() and sb == s and bb == b, name

@@ -236,3 +236,67 @@ def test_append_validates_before_writing():
     with pytest.raises(oracle.OracleError):
         c.append(x, np.ones_like(x), np.array([0], np.int32))
     assert (c.k_codes == 0).all() and (c.k_scales == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Bit-for-bit pins against the independent numpy-float32 statement
+# (tests/quant_reference.py), with no slack, and exact ties.
+
+import quant_reference as qref  # noqa: E402
+
+
+def _oracle_groups(X, bits):
+    """The oracle's quantizer over many groups at once (one append of N tokens)."""
+    N = X.shape[0]
+    c = oracle.Cache(1, 1, 64, N, bits, bits)
+    x = np.ascontiguousarray(X.reshape(1, 1, N, 64), np.float32)
+    c.append(x, x, np.zeros(1, np.int32))
+    return c.k_codes[0, 0, :, :], c.k_scales[0, 0, :, 0], c.k_biases[0, 0, :, 0]
+
+
+def random_groups(rng, count):
+    """Groups over many magnitudes and shapes: normal, one-signed, constant, near-constant."""
+    X = np.empty((count, 64), np.float32)
+    for i in range(count):
+        sc = 10.0 ** rng.uniform(-30, 30) if i % 11 == 0 else 10.0 ** rng.uniform(-4, 4)
+        x = rng.standard_normal(64) * sc
+        kind = i % 9
+        if kind == 1:
+            x = np.abs(x)
+        elif kind == 2:
+            x = -np.abs(x)
+        elif kind == 3:
+            x = np.full(64, x[0])
+        elif kind == 4:
+            x = x[0] + x * 1e-7
+        elif kind == 5:
+            x[rng.integers(0, 64, 8)] = x.max()
+        X[i] = np.clip(x, -1e38, 1e38).astype(np.float32)
+    return X
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bit_for_bit_against_numpy_float32(bits):
+    """20,000 random groups: codes, scales and biases identical, no tolerance."""
+    rng = np.random.default_rng(2024 + bits)
+    X = random_groups(rng, 20000)
+    oc, os_, ob = _oracle_groups(X, bits)
+    nc, ns, nb = qref.quantize_groups(X, bits)
+    assert (os_ == ns).all() and (ob == nb).all()
+    bad = np.nonzero((oc != nc).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} groups differ, first {bad[:5]}"
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_exact_ties_round_half_even(bits):
+    """Constructed groups with exact k + 1/2 ratios: the oracle rounds each to the
+    even neighbour (a closed form), and agrees bit for bit with the numpy statement
+    on the ties and their one-ulp neighbours."""
+    rng = np.random.default_rng(31 + bits)
+    X, E = qref.tie_groups(rng, bits, 2000)
+    oc, os_, ob = _oracle_groups(X, bits)
+    nc, ns, nb = qref.quantize_groups(X, bits)
+    known = E >= 0
+    assert known.sum() > 2000 * 40
+    assert (oc.astype(np.int64)[known] == E[known]).all()
+    assert (oc == nc).all() and (os_ == ns).all() and (ob == nb).all()
