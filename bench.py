@@ -2,22 +2,32 @@
 """Benchmark of quantized-KV attention on one MI355X.
 
 A step is one pass of the hot path over one batch of the workload: the step's
-new token(s) are quantized and appended to the cache (kvq_append_quantize),
-then the read runs (kvq_attn_decode / kvq_attn_prefill_chunk /
-kvq_attn_decode_shared).  Inputs are resident in HBM before timing starts.
+new token(s) are quantized and appended to the cache (kvq_append_quantize, or
+the fused kvq_decode_step on decode workloads), then the read runs
+(kvq_attn_decode / kvq_attn_prefill_chunk / kvq_attn_decode_shared /
+kvq_attn_mixed).  Inputs are resident in HBM before timing starts.
 
-To read HBM rather than the 256 MB last-level cache, every timed step reads
-one of several identical cache replicas in rotation, so that the rotation
-covers at least --rotate-gib of memory, and a 1 GiB buffer is read before
-each timed region.  The K timed steps are replayed from one HIP graph,
-so host launch overhead does not sit between them.
+To read HBM rather than the 256 MB last-level cache, every timed step reads one
+of several identical cache replicas in rotation, so that the rotation covers at
+least --rotate-gib of memory, and a 1 GiB buffer is read before each timed
+region.
 
-Output: one JSON line.  `value` is the headline workload's effective KV
-bandwidth (algorithmic bytes per step / time per step); `roofline` measures the
-attention call alone (split kernel + combine kernel, HIP events on the launch
-stream) against the 8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same workload; `configs` holds the same figures for
-every workload.
+Timing, all with HIP events on the launch stream:
+  * steps: K steps captured in one HIP graph and replayed (no host gaps between
+    launches); median, p10 and p90 over --reps replays of the per-step time;
+  * the attention call alone (main kernel + combine), the same way;
+  * the dominant kernel alone: K attention calls launched eagerly behind a GPU
+    sleep that holds the stream until all K are queued, each call asked
+    (kvq_mark_next_read) to record two events around its main kernel; median,
+    p10 and p90 over the K launches.  `roofline.achieved` uses this median.
+
+Output: one JSON line.  `value` is the headline workload's throughput per step
+(algorithmic bytes, or FLOPs for prefill, per step time); `roofline` is its
+dominant kernel against the published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16)
+and against the ceilings the probes measure on the same GPU (a stream read and
+an MFMA loop, include/kvq_probes.h); `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload; `configs` holds the same figures for every
+other workload.
 
 Algorithmic bytes per visible (key, KV head): K and V codes plus one bf16
 scale and one bf16 bias per 64-group for K and for V (an unquantized bf16
@@ -39,7 +49,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HEADLINE = "sliding_decode_b8_w512"
+# the largest configuration: three layers over a sliding donor plus a full
+# 16384-token head_dim-512 layer, batch 32, in one launch (581 MB per read)
+HEADLINE = "shared_decode_b32"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode attention effective KV GB/s (% of HBM peak); prefill TFLOP/s"
@@ -225,10 +237,10 @@ class Runner:
                 self.attend(r)
         return g
 
-    def run(self, steps, warmup, reps=3):
+    def run(self, steps, warmup, reps=7):
         """Time `steps` steps replayed from a HIP graph (no host gaps between
         launches), after flushing the last-level cache; also time the attention
-        calls alone the same way.  Median over `reps` replays of each."""
+        calls alone the same way.  Per-step time of each of `reps` replays."""
         torch = self.torch
         for i in range(warmup):
             self.append(i % self.nrep)
@@ -239,15 +251,10 @@ class Runner:
         g_step = self._graph(steps, warmup, "step")
         g_two = self._graph(steps, warmup, "two") if self.fused else None
         g_attn = self._graph(steps, warmup, "attn")
-        # Evict the last-level cache by reading 1 GiB: a read leaves clean lines,
-        # whereas a write fill would leave dirty ones whose write-back would be
-        # charged to the first timed steps.
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
-        sink = torch.empty(1, dtype=torch.float32, device="cuda")
         stream = torch.cuda.current_stream()
 
-        def timed(graph, k):
-            torch.sum(flush, dim=0, out=sink[0])
+        def timed(graph):
+            flush_llc()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             graph.replay()
@@ -255,21 +262,84 @@ class Runner:
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / steps
 
-        step_ms = float(np.median([timed(g_step, k) for k in range(reps)]))
-        attn_ms = float(np.median([timed(g_attn, k) for k in range(reps)]))
-        self.two_call_ms = float(np.median([timed(g_two, k) for k in range(reps)])) if g_two else None
-        del flush, g_step, g_attn, g_two
-        return step_ms, attn_ms
+        self.step_ms = [timed(g_step) for _ in range(reps)]
+        self.attn_ms = [timed(g_attn) for _ in range(reps)]
+        self.two_ms = [timed(g_two) for _ in range(reps)] if g_two else None
+        del g_step, g_attn, g_two
+        self.kernel_ms = self.kernel_events(steps)
+
+    def kernel_events(self, steps):
+        """Duration of each of `steps` launches of the read's main kernel, from the
+        two events the library records around it (kvq_mark_next_read).  The calls
+        are queued behind a GPU sleep, so no host gap falls inside a launch's pair."""
+        torch, kvq = self.torch, self.kvq
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:                              # create the handles
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        flush_llc()
+        torch.cuda._sleep(gate_cycles(steps * 0.3))   # ~0.3 ms of host time per queued call
+        for i, (a, b) in enumerate(evs):
+            kvq.kvq_mark_next_read(a, b)
+            self.attend(i % self.nrep)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
 
 
-def cpu_baseline(wl, runner, budget_s=10.0):
+_FLUSH = {}
+_GATE = {}
+
+
+def flush_llc():
+    """Evict the last-level cache by reading 1 GiB: a read leaves clean lines,
+    whereas a write fill would leave dirty ones whose write-back would be charged
+    to the first timed launches."""
+    import torch
+    if "buf" not in _FLUSH:
+        _FLUSH["buf"] = torch.ones(1 << 28, dtype=torch.float32, device="cuda")    # 1 GiB
+        _FLUSH["sink"] = torch.empty(1, dtype=torch.float32, device="cuda")
+    torch.sum(_FLUSH["buf"], dim=0, out=_FLUSH["sink"][0])
+
+
+def gate_cycles(ms: float) -> int:
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about `ms` ms
+    (its spin counts the GPU's clock, calibrated once)."""
+    import torch
+    if "per_ms" not in _GATE:
+        torch.cuda.synchronize()
+        n = 1 << 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        _GATE["per_ms"] = n / max(e0.elapsed_time(e1), 1e-3)
+    return int(_GATE["per_ms"] * max(ms, 1.0))
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, runner, budget_s):
     """Time the CPU oracle on the same workload: quantize-and-append of the step's
-    tokens plus the fp64 read of every query row.  Batch rows are sampled only
-    when the whole batch would be too slow for a short run; the time is then
-    scaled to the full batch."""
+    tokens plus the fp64 read of every query row, repeated for about `budget_s`
+    seconds.  Batch rows are sampled (row 0 only, time scaled by the batch) when
+    the whole batch would be too slow for a short run."""
     import oracle
     nthreads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    byts, _ = algorithmic(wl)
+    byts, flops = algorithmic(wl)
     B = wl.caches[0].B
     work = sum(s.B * min(s.length, s.window or s.length) * s.D for s in wl.caches)
     nb = B if work <= 64e6 else 1
@@ -294,48 +364,129 @@ def cpu_baseline(wl, runner, budget_s=10.0):
         t_total += time.perf_counter() - t
         n += 1
     step_s = t_total / n * (B / nb)
+    model, affinity = host_cpu()
     rows = "all %d batch rows" % B if nb == B else "batch row 0 of %d, time scaled x%d" % (B, B)
-    return {"value": round(byts / step_s / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+    if wl.kind == "prefill":
+        value, unit = flops / step_s / 1e12, "TFLOP/s"
+    else:
+        value, unit = byts / step_s / 1e9, "GB/s"
+    return {"value": round(value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
             "sample": f"{n} full oracle steps ({t_total:.1f} s) on {rows}: fp32 quantize-append of the "
-                      f"step's tokens + fp64 attention of every query row"}
+                      f"step's tokens + fp64 attention of every query row",
+            "s_per_step": round(step_s, 6), "cpu_model": model, "affinity_cpus": affinity}
 
 
-def measure(name, steps, warmup, rotate_gib, with_cpu):
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def probe_ceilings():
+    """Attainable HBM read rate and dense bf16 MFMA rate on this GPU, from the
+    probes of include/kvq_probes.h (best over a few launch shapes, 3 runs each)."""
+    import torch
+    from decode_attention_group_amd import probes
+    stream = torch.cuda.current_stream()
+
+    def time_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    nbytes = 4 << 30                                  # 16x the last-level cache
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    best_read, read_cfg, read_sweep = 0.0, None, []
+    for blocks in (512, 1024, 2048, 4096, 8192):
+        for nt in (0, 1):
+            probes.stream_read(src, blocks, bool(nt), sink)          # warm-up
+            ms = min(time_ms(lambda: probes.stream_read(src, blocks, bool(nt), sink)) for _ in range(3))
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            read_sweep.append([blocks, nt, round(gbs, 1)])
+            if gbs > best_read:
+                best_read, read_cfg = gbs, {"blocks": blocks, "nontemporal": nt}
+    del src
+    fsink = torch.empty(4096 * 256, dtype=torch.float32, device="cuda")
+    best_mfma, mfma_cfg, mfma_sweep = 0.0, None, []
+    for shape in (0, 1):
+        for blocks in (1024, 2048, 4096):
+            iters = 2000
+            probes.mfma_bf16(shape, 10, blocks, fsink)
+            flops = 0.0
+
+            def run():
+                nonlocal flops
+                flops = probes.mfma_bf16(shape, iters, blocks, fsink)
+            ms = min(time_ms(run) for _ in range(3))
+            tf = flops / (ms * 1e-3) / 1e12
+            mfma_sweep.append([shape, blocks, round(tf, 1)])
+            if tf > best_mfma:
+                best_mfma, mfma_cfg = tf, {"mfma": "16x16x32" if shape == 0 else "32x32x16", "blocks": blocks}
+    torch.cuda.synchronize()
+    return {"hbm_read_gbs": round(best_read, 1), "hbm_read_probe": read_cfg,
+            "mfma_bf16_tflops": round(best_mfma, 1), "mfma_probe": mfma_cfg,
+            "hbm_read_sweep [blocks, nontemporal, GB/s]": read_sweep,
+            "mfma_sweep [shape 0=16x16x32 1=32x32x16, blocks, TFLOP/s]": mfma_sweep}
+
+
+def measure(name, steps, warmup, rotate_gib, cpu_s, ceilings):
     import synth
     wl = synth.WORKLOADS[name]
-    runner = Runner(wl, rotate_gib * (1 << 30), keep_oracle=with_cpu)
-    step_ms, attn_ms = runner.run(steps, warmup)
+    runner = Runner(wl, rotate_gib * (1 << 30), keep_oracle=cpu_s > 0)
+    runner.run(steps, warmup)
     byts, flops = algorithmic(wl)
-    res = {"workload": name, "ms_per_step": step_ms, "attn_ms": attn_ms, "bytes": byts, "flops": flops,
-           "replicas": runner.nrep, "fused_step": runner.fused,
-           "two_call_ms_per_step": None if runner.two_call_ms is None else round(runner.two_call_ms, 5)}
+    step_ms, attn_ms, kern_ms = (float(np.median(x)) for x in (runner.step_ms, runner.attn_ms, runner.kernel_ms))
+    res = {"workload": name, "ms_per_step": step_ms,
+           "step_p10_ms": pct(runner.step_ms, 10), "step_p90_ms": pct(runner.step_ms, 90),
+           "attn_ms": attn_ms, "bytes": byts, "flops": flops, "replicas": runner.nrep, "fused_step": runner.fused,
+           "two_call_ms_per_step": None if runner.two_ms is None else round(float(np.median(runner.two_ms)), 5)}
     if wl.kind == "prefill":
-        res.update(value=flops / (step_ms * 1e-3) / 1e12, unit="TFLOP/s",
-                   roofline={"bound": "mfma", "achieved": round(flops / (attn_ms * 1e-3) / 1e12, 3),
-                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)})
+        work, scale, unit, peak, ceil, bound = flops, 1e12, "TFLOP/s", BF16_PEAK_TFLOPS, ceilings.get(
+            "mfma_bf16_tflops"), "mfma"
     else:
-        res.update(value=byts / (step_ms * 1e-3) / 1e9, unit="GB/s",
-                   roofline={"bound": "hbm", "achieved": round(byts / (attn_ms * 1e-3) / 1e9, 2),
-                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(byts / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5)})
-    res["roofline"]["traffic"] = measured_traffic(name)
-    if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, runner)
+        work, scale, unit, peak, ceil, bound = byts, 1e9, "GB/s", HBM_PEAK_GBS, ceilings.get("hbm_read_gbs"), "hbm"
+    rate = lambda ms: work / (ms * 1e-3) / scale  # noqa: E731
+    achieved = rate(kern_ms)
+    res.update(value=rate(step_ms), unit=unit)
+    res["roofline"] = {
+        "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+        "frac": round(achieved / peak, 5), "traffic": measured_traffic(name),
+        "kernel": dominant_kernel_name(name), "kernel_ms": round(kern_ms, 6),
+        "kernel_p10_ms": round(pct(runner.kernel_ms, 10), 6), "kernel_p90_ms": round(pct(runner.kernel_ms, 90), 6),
+        "kernel_launches": len(runner.kernel_ms),
+        "measured_ceiling": ceil, "frac_of_measured_ceiling": round(achieved / ceil, 5) if ceil else None,
+        "call_achieved": round(rate(attn_ms), 3), "call_frac": round(rate(attn_ms) / peak, 5),
+        "call_frac_of_measured_ceiling": round(rate(attn_ms) / ceil, 5) if ceil else None,
+    }
+    if cpu_s > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, runner, cpu_s)
     del runner
     import torch
     torch.cuda.empty_cache()
     return res
 
 
+def dominant_kernel_name(name):
+    try:
+        with open(PROFILES) as f:
+            return json.load(f)["workloads"][name]["kernel"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="measure only --workload")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-probes", action="store_true", help="skip the ceiling probes")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the headline")
+    ap.add_argument("--cpu-seconds-other", type=float, default=3.0, help="oracle time budget for other configs")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times (reference kernel for "
@@ -358,22 +509,44 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}))
         return
-    head = measure(args.workload, args.steps, args.warmup, args.rotate_gib, not args.no_cpu)
+    ceilings = {} if args.no_probes else probe_ceilings()
+    if ceilings:
+        print(f"# probes: {json.dumps(ceilings)}", file=sys.stderr, flush=True)
+    cpu_head = 0.0 if args.no_cpu else args.cpu_seconds
+    cpu_other = 0.0 if args.no_cpu else args.cpu_seconds_other
+
+    def summary(r):
+        rf = r["roofline"]
+        print(f"# {r['workload']}: {r['value']:.2f} {r['unit']} step {r['ms_per_step'] * 1e3:.1f} us, call "
+              f"{r['attn_ms'] * 1e3:.1f} us, kernel {rf['kernel_ms'] * 1e3:.1f} us = {rf['achieved']} {rf['unit']} "
+              f"({100 * rf['frac']:.1f}% of peak, "
+              f"{'-' if rf['frac_of_measured_ceiling'] is None else round(100 * rf['frac_of_measured_ceiling'], 1)}"
+              f"% of measured)", file=sys.stderr, flush=True)
+
+    head = measure(args.workload, args.steps, args.warmup, args.rotate_gib, cpu_head, ceilings)
+    summary(head)
     others = {}
     if not args.only:
         for name in synth.WORKLOADS:
             if name == args.workload:
                 continue
-            r = measure(name, args.steps, args.warmup, args.rotate_gib, False)
-            others[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "attn_ms", "replicas",
-                                              "two_call_ms_per_step")}
-            others[name]["roofline_frac"] = r["roofline"]["frac"]
-            others[name]["achieved"] = r["roofline"]["achieved"]
-            print(f"# {name}: {r['value']:.2f} {r['unit']} step {r['ms_per_step'] * 1e3:.1f} us, "
-                  f"attention {r['attn_ms'] * 1e3:.1f} us = {r['roofline']['achieved']} {r['roofline']['unit']} "
-                  f"({100 * r['roofline']['frac']:.1f}% of peak)", file=sys.stderr, flush=True)
+            r = measure(name, args.steps, args.warmup, args.rotate_gib, cpu_other, ceilings)
+            summary(r)
+            others[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "step_p10_ms", "step_p90_ms",
+                                              "attn_ms", "replicas", "two_call_ms_per_step", "roofline")
+                            if k in r}
+            if "cpu_baseline" in r:
+                others[name]["cpu_baseline"] = r["cpu_baseline"]
     wl = synth.WORKLOADS[args.workload]
-    spec = wl.caches[0]
+    config = {"workload": args.workload, "description": wl.description, "batch": wl.caches[0].B,
+              "caches": [{"name": c.name, "head_dim": c.D, "kv_heads": c.Hkv, "k_bits": c.k_bits,
+                          "v_bits": c.v_bits, "window": c.window, "capacity": c.R, "cached_tokens": c.length}
+                         for c in wl.caches],
+              "queries": [{"cache": q.cache, "layers": q.layers, "q_heads": q.Hq, "chunk": q.C} for q in wl.queries],
+              "replicas": head["replicas"],
+              "step": ("kvq_decode_step: the token's append and the attention read in one call"
+                       if head["fused_step"] else "append the step's token(s) + attention read"),
+              "compute": "4/8-bit codes -> fp16 MFMA, fp32 accumulate, bf16 out"}
     line = {
         "metric": METRIC,
         "value": round(head["value"], 3),
@@ -381,21 +554,19 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms_per_step"], 5),
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "step_p10_ms": round(head["step_p10_ms"], 6),
+        "step_p90_ms": round(head["step_p90_ms"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": spec.B, "head_dim": spec.D, "q_heads": wl.queries[0].Hq,
-                   "kv_heads": spec.Hkv, "k_bits": spec.k_bits, "v_bits": spec.v_bits, "window": spec.window,
-                   "cached_tokens": spec.length, "replicas": head["replicas"],
-                   "step": ("kvq_decode_step: the token's append and the attention read in one call"
-                            if head["fused_step"] else "append the step's token(s) + attention read"),
-                   "compute": "4/8-bit codes -> fp16 MFMA, fp32 accumulate, bf16 out"},
+        "config": config,
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
-        "attn_ms": round(head["attn_ms"], 5),
+        "ceilings": ceilings,
+        "attn_ms": round(head["attn_ms"], 6),
         "two_call_ms_per_step": head["two_call_ms_per_step"],
         "configs": others,
     }

@@ -14,6 +14,7 @@ Functions (same names as the C entry points):
   kvq_attn_mixed(reads, workspace=None)
   kvq_decode_workspace_bytes(groups), kvq_decode_step_workspace_bytes(...),
   kvq_mixed_workspace_bytes(reads), kvq_prefill_workspace_bytes(...)
+  kvq_mark_next_read(before, after)   (measurement: events around the next read's main kernel)
 """
 from __future__ import annotations
 
@@ -39,7 +40,7 @@ SIZE_MAX = (1 << 64) - 1
 EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
            "kvq_attn_decode_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
            "kvq_decode_step_workspace_bytes", "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
-           "kvq_last_error")
+           "kvq_last_error", "kvq_mark_next_read")
 
 
 class KvqUnavailable(RuntimeError):
@@ -105,6 +106,8 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_decode_workspace_bytes.restype = sz
     lib.kvq_prefill_workspace_bytes.argtypes = [CP, i32, i32, i32]
     lib.kvq_prefill_workspace_bytes.restype = sz
+    lib.kvq_mark_next_read.argtypes = [P, P]
+    lib.kvq_mark_next_read.restype = ctypes.c_int
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     for name in ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
@@ -173,6 +176,19 @@ class KVCache:
 
     def nbytes(self) -> int:
         return sum(t.numel() * 4 for t in (self.k_codes, self.v_codes, self.k_sb, self.v_sb) if t is not None)
+
+
+def kvq_mark_next_read(before: Optional["torch.cuda.Event"], after: Optional["torch.cuda.Event"]):
+    """Arm two torch.cuda.Events (already recorded once, so that they exist) for the next
+    attention call on this thread: it records them around its main kernel."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("record the event once before arming it")
+        return h
+    _check(load_library().kvq_mark_next_read(handle(before), handle(after)))
 
 
 def kvq_append_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: torch.Tensor):

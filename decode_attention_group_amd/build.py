@@ -9,6 +9,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["append.hip", "attn.hip", "prefill.hip", "prefill_codes.hip", "bf16_cache.hip", "kvq_api.hip"]
+# measurement probes (include/kvq_probes.h), a library of their own
+PROBE_LIB = os.path.join(HERE, "libkvq_probes.so")
+PROBE_SOURCES = ["probes.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,22 +26,31 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    objs = []
-    for src in SOURCES:
+def _link(sources, lib, verbose):
+    """Compile the sources in parallel (one hipcc per file), then link them."""
+    procs, objs = [], []
+    for src in sources:
         obj = os.path.join(CSRC, src.replace(".hip", ".o"))
         cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        procs.append((cmd, subprocess.Popen(cmd)))
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

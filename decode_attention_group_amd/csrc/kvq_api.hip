@@ -16,6 +16,25 @@
 namespace {
 
 thread_local char g_err[512] = "";
+// kvq_mark_next_read: events the next attention call records around its main kernel
+thread_local hipEvent_t g_mark_before = nullptr;
+thread_local hipEvent_t g_mark_after = nullptr;
+
+void mark_before(hipStream_t stream)
+{
+    if (g_mark_before) (void)hipEventRecord(g_mark_before, stream);
+    g_mark_before = nullptr;
+}
+
+void mark_after(hipStream_t stream)
+{
+    if (g_mark_after) (void)hipEventRecord(g_mark_after, stream);
+}
+
+// Every attention call ends its marks (armed for one call only).
+struct MarkScope {
+    ~MarkScope() { g_mark_before = g_mark_after = nullptr; }
+};
 
 kvq_status fail(kvq_status st, const char* fmt, ...)
 {
@@ -257,6 +276,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
                     what, i, P.d[i].B, P.d[i].Hkv, P.d[i].Hq, P.d[i].D, P.d[i].R, P.d[i].W, P.d[i].C,
                     P.d[i].n_rows, P.d[i].n_rt, P.d[i].S, P.d[i].split_len, P.d[i].n_items);
     hipError_t e = hipSuccess;
+    mark_before(stream);
     if (same) {
         e = launch_one(P, total_items);
     } else if (big) {
@@ -272,6 +292,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
             e = launch_one(one, P.d[i].n_items);
         }
     }
+    mark_after(stream);
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
@@ -280,6 +301,13 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
 }  // namespace
 
 KVQ_API const char* kvq_last_error(void) { return g_err; }
+
+KVQ_API kvq_status kvq_mark_next_read(hipEvent_t before, hipEvent_t after)
+{
+    g_mark_before = before;
+    g_mark_after = after;
+    return ok();
+}
 
 KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, const float* v,
                                        int32_t T, const int32_t* pos0, hipStream_t stream)
@@ -517,6 +545,7 @@ KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, in
                                    const int32_t* len, int32_t max_len, float scale, uint16_t* out,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    MarkScope marks;
     const char* what = "kvq_attn_decode";
     const uint16_t* qs[1] = {q};
     uint16_t* os[1] = {out};
@@ -543,6 +572,7 @@ KVQ_API kvq_status kvq_decode_step(const kvq_cache* cache, const float* k, const
                                    uint16_t* out, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream)
 {
+    MarkScope marks;
     const char* what = "kvq_decode_step";
     const uint16_t* qs[1] = {q};
     uint16_t* os[1] = {out};
@@ -560,6 +590,7 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
                                           uint16_t* out, void* workspace, size_t workspace_bytes,
                                           hipStream_t stream)
 {
+    MarkScope marks;
     const char* what = "kvq_attn_prefill_chunk";
     const uint16_t* qs[1] = {q};
     uint16_t* os[1] = {out};
@@ -579,7 +610,9 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
             fprintf(stderr, "[kvq] %s short-chunk kernel: B=%d Hkv=%d Hq=%d D=%d C=%d rows=%d S=%d split=%d wg=%d\n",
                     what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].C, P.d[0].n_rows, P.d[0].S,
                     P.d[0].split_len, total_items);
+        mark_before(stream);
         hipError_t e = kvq::launch_prefill_codes(P, total_items, stream);
+        mark_after(stream);
         if (e == hipSuccess) e = kvq::launch_combine(P, stream);
         if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
         return ok();
@@ -589,7 +622,12 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
         fprintf(stderr, "[kvq] %s prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d split=%d wg=%d band=%d\n",
                 what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].R, P.d[0].W, P.d[0].C, P.d[0].n_rows,
                 P.d[0].S, P.d[0].split_len, total_items, P.d[0].nk);
-    hipError_t e = kvq::launch_prefill(P, total_items, stream);
+    hipError_t e = kvq::launch_band(P, stream);
+    if (e == hipSuccess) {
+        mark_before(stream);
+        e = kvq::launch_prefill(P, total_items, stream);
+        mark_after(stream);
+    }
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
@@ -607,6 +645,7 @@ KVQ_API size_t kvq_mixed_workspace_bytes(const kvq_read* reads, int32_t n_reads)
 KVQ_API kvq_status kvq_attn_mixed(const kvq_read* reads, int32_t n_reads, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream)
 {
+    MarkScope marks;
     const char* what = "kvq_attn_mixed";
     ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
     kvq_status st = mixed_specs(reads, n_reads, rs, what, false);
@@ -617,6 +656,7 @@ KVQ_API kvq_status kvq_attn_mixed(const kvq_read* reads, int32_t n_reads, void* 
 KVQ_API kvq_status kvq_attn_decode_shared(const kvq_shared_group* groups, int32_t n_groups,
                                           void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
+    MarkScope marks;
     const char* what = "kvq_attn_decode_shared";
     if (!groups) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: groups is NULL", what);
     if (n_groups < 1 || n_groups > KVQ_MAX_SHARED_GROUPS)

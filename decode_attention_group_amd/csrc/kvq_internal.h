@@ -88,6 +88,9 @@ hipError_t launch_append_bf16(const AppendParams& p, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
+// The chunk's band tiles (dequantized, or a bf16 copy) when the prefill kernel
+// needs them; then the prefill kernel itself.
+hipError_t launch_band(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_t stream);
 

@@ -651,7 +651,7 @@ __global__ __launch_bounds__(64 * pf_waves<D>()) void prefill_kernel(AttnParams 
     prefill_body<D, DIRECT>(P.d[0], xcd_item(blockIdx.x, gridDim.x), sm);
 }
 
-hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream)
+hipError_t launch_band(const AttnParams& p, hipStream_t stream)
 {
     const AttnDesc& d = p.d[0];
     const dim3 dq_grid(d.nk / kStep, d.Hkv, d.B), block(256);
@@ -670,8 +670,12 @@ hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stre
         break;
     default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream)
+{
+    const AttnDesc& d = p.d[0];
     const bool direct = cfg_is_bf16(d.cfg) && d.band == nullptr;
     const dim3 grid(total_items);
     if (d.D == 256) {

@@ -292,6 +292,19 @@ size_t kvq_decode_step_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads
 size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads,
                                    int32_t chunk, int32_t max_len);
 
+/*
+ * (host) Measurement: arm two events for the next attention call made on this
+ * thread (kvq_attn_decode, kvq_decode_step, kvq_attn_prefill_chunk,
+ * kvq_attn_decode_shared or kvq_attn_mixed).  That call records `before` on its
+ * stream just before it launches its main kernel (the split read, the prefill
+ * kernel or the short-chunk kernel: not a band copy and not the combine of the
+ * split partials) and `after` just after it, so hipEventElapsedTime(before,
+ * after) is the main kernel's time on the stream.  Either event may be NULL.
+ * The marks are used by that one call, whether or not it launches anything, and
+ * then dropped.  Events are caller-created; nothing else changes.
+ */
+kvq_status kvq_mark_next_read(hipEvent_t before, hipEvent_t after);
+
 /* (host) Message for the last non-OK status on this thread ("" if none). */
 const char *kvq_last_error(void);
 

@@ -34,6 +34,30 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_every_declared_symbol():
+    """include/kvq_probes.h (the measurement probes) against libkvq_probes.so."""
+    from decode_attention_group_amd import probes
+    if not os.path.exists(probes.LIB_PATH):
+        pytest.skip("libkvq_probes.so not built")
+    text = open(os.path.join(ROOT, "include", "kvq_probes.h")).read()
+    names = set(re.findall(r"^\s*(?:int|double)\s*(kvq_\w+)\s*\(", text, re.M))
+    assert names == set(probes.EXPORTS)
+    so = probes.load_library()
+    for n in names:
+        assert hasattr(so, n), n
+    # argument checks need no GPU: nothing is launched on a bad argument
+    assert so.kvq_probe_stream_read(None, 16, 1, 0, FAKE, None) == 1
+    assert so.kvq_probe_stream_read(FAKE + 4, 16, 1, 0, FAKE, None) == 1
+    assert so.kvq_probe_mfma_bf16(2, 1, 1, FAKE, None) == 1
+    assert so.kvq_probe_mfma_flops_per_iter(0, 2) == 8 * 2 * 16 * 16 * 32 * 4 * 2
+
+
+def test_mark_next_read_needs_no_gpu(lib):
+    """Arming NULL events is valid; the next (failing) call drops the marks."""
+    assert lib.kvq_mark_next_read(None, None) == 0
+    assert decode(lib, cache(head_dim=100)) == 2
+
+
 def cache(**kw):
     c = dict(k_codes=FAKE, v_codes=FAKE, k_sb=FAKE, v_sb=FAKE, batch=2, n_kv_heads=2, head_dim=256,
              group_size=64, k_bits=4, v_bits=8, capacity=512, window=512)
