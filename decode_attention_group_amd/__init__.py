@@ -40,7 +40,8 @@ SIZE_MAX = (1 << 64) - 1
 EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
            "kvq_attn_decode_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
            "kvq_decode_step_workspace_bytes", "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
-           "kvq_last_error", "kvq_mark_next_read")
+           "kvq_last_error", "kvq_mark_next_read", "kvq_attn_decode_static")
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class KvqUnavailable(RuntimeError):
@@ -106,6 +107,8 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_decode_workspace_bytes.restype = sz
     lib.kvq_prefill_workspace_bytes.argtypes = [CP, i32, i32, i32]
     lib.kvq_prefill_workspace_bytes.restype = sz
+    lib.kvq_attn_decode_static.argtypes = [CP, P, i32, P, i32, ctypes.c_float, P, P]
+    lib.kvq_attn_decode_static.restype = ctypes.c_int
     lib.kvq_mark_next_read.argtypes = [P, P]
     lib.kvq_mark_next_read.restype = ctypes.c_int
     lib.kvq_last_error.argtypes = []
@@ -254,6 +257,21 @@ def kvq_attn_decode(cache: KVCache, q: torch.Tensor, len_: torch.Tensor, max_len
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.kvq_attn_decode(ctypes.byref(cache.struct), _ptr(q), q.shape[1], _ptr(len_), int(max_len),
                                float(scale), _ptr(out), _ptr(ws), wsb, _stream()))
+    return out
+
+
+def kvq_attn_decode_static(cache: KVCache, q: torch.Tensor, len_: torch.Tensor, max_len: int,
+                           scale: float = 1.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kvq_attn_decode with the library's static device scratch instead of a workspace
+    (no allocation inside the call; `out` must be given by callers that cannot allocate)."""
+    lib = load_library()
+    _gpu(q, "q", torch.bfloat16)
+    _gpu(len_, "len", torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _gpu(out, "out", torch.bfloat16)
+    _check(lib.kvq_attn_decode_static(ctypes.byref(cache.struct), _ptr(q), q.shape[1], _ptr(len_), int(max_len),
+                                      float(scale), _ptr(out), _stream()))
     return out
 
 

@@ -8,10 +8,17 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kvq_internal.h"
 
 #define KVQ_API extern "C" __attribute__((visibility("default")))
+
+// Split partials of kvq_attn_decode_static, for callers that cannot allocate:
+// one copy of this array per device, held until the process ends.  Host code
+// never uses its name as an address: the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[KVQ_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -298,6 +305,32 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     return ok();
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept.
+kvq_status static_scratch(void** ptr, const char* what)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", what, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KVQ_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", what,
+                        dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return KVQ_OK;
+}
+
 }  // namespace
 
 KVQ_API const char* kvq_last_error(void) { return g_err; }
@@ -553,6 +586,31 @@ KVQ_API kvq_status kvq_attn_decode(const kvq_cache* cache, const uint16_t* q, in
     kvq_status st = check_read(r, what);
     if (st != KVQ_OK) return st;
     return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
+}
+
+KVQ_API kvq_status kvq_attn_decode_static(const kvq_cache* cache, const uint16_t* q, int32_t n_q_heads,
+                                          const int32_t* len, int32_t max_len, float scale, uint16_t* out,
+                                          hipStream_t stream)
+{
+    MarkScope marks;
+    const char* what = "kvq_attn_decode_static";
+    const uint16_t* qs[1] = {q};
+    uint16_t* os[1] = {out};
+    ReadSpec r{cache, 1, qs, os, n_q_heads, scale, len, max_len, 1};
+    kvq_status st = check_read(r, what);
+    if (st != KVQ_OK) return st;
+    kvq::AttnParams P;
+    int total = 0;
+    const size_t need = plan_all(&r, 1, P, total);
+    if (need > (size_t)KVQ_STATIC_SCRATCH_BYTES)
+        return fail(KVQ_ERR_WORKSPACE, "%s: this read needs %zu bytes of split partials, more than the %d-byte "
+                    "static scratch; use kvq_attn_decode with a workspace", what, need, KVQ_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+        st = static_scratch(&ws, what);
+        if (st != KVQ_OK) return st;
+    }
+    return run_reads(&r, 1, ws, KVQ_STATIC_SCRATCH_BYTES, stream, what);
 }
 
 KVQ_API size_t kvq_decode_step_workspace_bytes(const kvq_cache* cache, int32_t n_q_heads, int32_t max_len)

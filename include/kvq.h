@@ -84,6 +84,7 @@ typedef enum {
 #define KVQ_MIN_CAPACITY 32        /* smallest cache capacity (one 32-key read step)     */
 #define KVQ_MAX_SHARED_LAYERS 16   /* layers per kvq_shared_group                       */
 #define KVQ_MAX_SHARED_GROUPS 4    /* groups per kvq_attn_decode_shared call             */
+#define KVQ_STATIC_SCRATCH_BYTES (32 << 20)  /* device scratch of kvq_attn_decode_static  */
 
 /*
  * (host) Descriptor of one layer's cache.  R = capacity slots; a token at
@@ -172,6 +173,30 @@ kvq_status kvq_attn_decode(const kvq_cache *cache,
                            uint16_t *out,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/*
+ * kvq_attn_decode for callers that cannot allocate device memory and cannot
+ * pass a workspace: code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation.  Same arguments, same kernels and the same result
+ * as kvq_attn_decode, minus the workspace: the split partials go to a static
+ * device array of KVQ_STATIC_SCRATCH_BYTES (32 MiB) inside this library, one
+ * per device, allocated with the library's code on that device and held until
+ * the process ends.  The call allocates nothing.  The stream must belong to
+ * the current device.
+ * A read whose partials need more than KVQ_STATIC_SCRATCH_BYTES (the size
+ * kvq_decode_workspace_bytes reports for the same arguments; the split plan
+ * aims at about 512 workgroups of 16 rows, so a head_dim-512 read needs at
+ * most about 33 MB and most reads far less) returns KVQ_ERR_WORKSPACE and
+ * launches nothing.
+ * All calls on one device share that device's array: two of these calls that
+ * overlap in time on one device (different streams, no ordering between them)
+ * race and give wrong results; calls ordered on one stream are safe.  The
+ * array needs no clearing between calls.
+ */
+kvq_status kvq_attn_decode_static(const kvq_cache *cache,
+                                  const uint16_t *q, int32_t n_q_heads,
+                                  const int32_t *len, int32_t max_len, float scale,
+                                  uint16_t *out, hipStream_t stream);
 
 /*
  * One decode step of a layer: append this step's token of every sequence and

@@ -262,3 +262,16 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_static_decode_validation(lib, monkeypatch):
+    """The allocation-free decode read validates like kvq_attn_decode and refuses a
+    read whose partials exceed its static scratch, before touching the GPU."""
+    c = cache(head_dim=100)
+    assert lib.kvq_attn_decode_static(ctypes.byref(c), FAKE, 8, FAKE, 4096, 1.0, FAKE, None) == 2
+    c = cache()
+    assert lib.kvq_attn_decode_static(ctypes.byref(c), None, 8, FAKE, 4096, 1.0, FAKE, None) == 1
+    monkeypatch.setenv("KVQ_SPLITS", "128")
+    c = cache(batch=64, n_kv_heads=1, head_dim=512, k_bits=8, v_bits=8, capacity=32768, window=0)
+    assert lib.kvq_attn_decode_static(ctypes.byref(c), FAKE, 8, FAKE, 32768, 1.0, FAKE, None) == 4
+    assert "static scratch" in lib.kvq_last_error().decode()
