@@ -230,11 +230,29 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         total += bytes[i];
     }
     const int kTargetWg = 512;   // two 4-wave workgroups per CU on 256 CUs
+    // A descriptor with at least as many work items (one split each) as its
+    // share of the target keeps that many; the rest of the target is shared by
+    // the others in proportion to their bytes, so that the launch stays within
+    // what the chip holds at once (a second wave of workgroups would start the
+    // longest items late).
+    int fixed_wg = 0;
+    double free_bytes = 0.0;
+    bool fixed[KVQ_MAX_SHARED_GROUPS];
+    for (int i = 0; i < n; ++i) {
+        const kvq_cache* c = rs[i].cache;
+        const int rows = (rs[i].C == 1 ? rs[i].n_layers : rs[i].C) * (rs[i].Hq / c->n_kv_heads);
+        const int64_t items = (int64_t)c->batch * c->n_kv_heads * ((rows + kvq::kRowTile - 1) / kvq::kRowTile);
+        fixed[i] = total > 0 && items >= kTargetWg * (bytes[i] / total);
+        if (fixed[i]) fixed_wg += (int)std::min<int64_t>(items, kTargetWg);
+        else free_bytes += bytes[i];
+    }
+    const int free_wg = std::max(kTargetWg / 4, kTargetWg - fixed_wg);
     total_items = 0;
     int comb = 0;
     size_t ws = 0;
     for (int i = 0; i < n; ++i) {
-        const int target = std::max(1, (int)std::lround(kTargetWg * (total > 0 ? bytes[i] / total : 1.0)));
+        const double share = fixed[i] ? 0.0 : (free_bytes > 0 ? bytes[i] / free_bytes : 1.0);
+        const int target = std::max(1, (int)std::lround(free_wg * share));
         kvq::AttnDesc& d = P.d[i];
         plan_read(rs[i], target, d);
         d.item_begin = total_items;
