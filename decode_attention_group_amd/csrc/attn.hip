@@ -266,6 +266,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     // ---- q of this wave's groups as MFMA B operand (fp16, element order matching
     //      the K code order); Q_g = sum of the group's q for the bias MFMA
     f16x8 qf[GPW][2];
+    float qinv[GPW];     // 2^-k: undoes the power of 2 that put each (row, group) of q in fp16 range
     bf16x8 qb;
     // q loads are unconditional (a lane past the last row reads row 0 of the
     // tile and zeroes it afterwards), so no branch forces an early wait.
@@ -292,10 +293,17 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
                 f[8 + 2 * e] = bf16_lo_to_f32(u1[e]);
                 f[8 + 2 * e + 1] = bf16_hi_to_f32(u1[e]);
             }
-            float acc = 0.0f;
+            float acc = 0.0f, amax = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc += f[e];
+            for (int e = 0; e < 16; ++e) { acc += f[e]; amax = fmaxf(amax, fabsf(f[e])); }
             const float Q = sum_across_groups(acc);
+            // The row's 64 values of this group enter the MFMA as fp16 after a power
+            // of 2 that puts their largest magnitude in [2^14, 2^15): bf16 -> fp16 is
+            // then exact for every value within 2^-28 of it, at any magnitude of q.
+            // The partial score is multiplied back by qinv (exact).
+            const uint32_t ex = min(max((__float_as_uint(max_across_groups(amax)) >> 23) & 0xFFu, 15u), 254u);
+            const float qmul = __uint_as_float((268u - ex) << 23);
+            qinv[gi] = __uint_as_float((ex - 14u) << 23);
             // Q in three bf16 parts: their sum carries ~24 bits of Q
             const float q1 = __uint_as_float((uint32_t)f32_to_bf16_rne(Q) << 16);
             const float q2 = __uint_as_float((uint32_t)f32_to_bf16_rne(Q - q1) << 16);
@@ -306,8 +314,8 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int e0 = KB == 8 ? e : nib_order(e);
-                qf[gi][0][e] = (_Float16)f[e0];
-                qf[gi][1][e] = (_Float16)f[8 + e0];
+                qf[gi][0][e] = (_Float16)(f[e0] * qmul);
+                qf[gi][1][e] = (_Float16)(f[8 + e0] * qmul);
             }
         }
         // bias k-slot k = (term*3 + part)*GPW + gi: term 0 pairs b with Q, term 1
@@ -416,7 +424,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
                 x = mfma_f16(a1, qf[gi][1], x);
                 const u32x4 sw = *reinterpret_cast<const u32x4*>(&sm.ksb[wave][gi][8 * lg + 4 * t]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sacc[i] += bf16_lo_to_f32(sw[i]) * x[i];
+                for (int i = 0; i < 4; ++i) sacc[i] += (bf16_lo_to_f32(sw[i]) * qinv[gi]) * x[i];
             }
             sm.spart[par][wave][t][lane] = sacc;
         }
@@ -465,6 +473,59 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     };
 
+    // ---- PV of one step with bf16 operands (any V scale and bias): every fp32
+    //      weight w (p, or p * s_v) enters as hi = bf16(w) plus lo = bf16(w - hi),
+    //      two MFMAs against the exact bf16 codes and biases (about 16 bits of w).
+    auto pv_wide = [&](const VRegs<D, VB>& vr, const float (&p)[8], const float (&pp)[8], const bool (&kin)[8],
+                       bool full) {
+        auto hi_of = [](float w) { return (__bf16)w; };
+        auto lo_of = [](float w) { return (__bf16)(w - (float)(__bf16)w); };
+        {
+            u32x4 w0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg]);
+            u32x4 w1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][m < GPW ? m : 0][8 * lg + 4]);
+            if (m >= GPW) { w0 = (u32x4)0; w1 = (u32x4)0; }
+            bf16x8 ac, ph, pl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = VB == 8 ? e : nib_order(e);
+                const uint32_t bw = k < 4 ? w0[k & 3] : w1[k & 3];
+                ac[e] = kin[k] ? (__bf16)bf16_hi_to_f32(bw) : (__bf16)0.0f;
+                ph[e] = hi_of(pp[k]);
+                pl[e] = lo_of(pp[k]);
+            }
+            f32x4 c = corr;
+            c = mfma_bf16(ac, ph, c);
+            corr = mfma_bf16(ac, pl, c);
+        }
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+            const u32x4 s0 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][gi][8 * lg]);
+            const u32x4 s1 = *reinterpret_cast<const u32x4*>(&sm.vsb[wave][gi][8 * lg + 4]);
+            bf16x8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = VB == 8 ? e : nib_order(e);
+                const float sv = bf16_lo_to_f32(k < 4 ? s0[k & 3] : s1[k & 3]);
+                const float w = full || p[k] >= 0.0f ? p[k] * sv : 0.0f;
+                bh[e] = hi_of(w);
+                bl[e] = lo_of(w);
+            }
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const int dt = 4 * gi + dd;
+                f16x8 a16;
+                if constexpr (VB == 8) a16 = codes8x8_to_f16(vr.vc[dt]);
+                else a16 = codes4x8_to_f16(vr.vc[dt]);
+                bf16x8 a;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = (__bf16)(float)a16[e];     // codes <= 255: exact
+                f32x4 o = O[dt];
+                o = mfma_bf16(a, bh, o);
+                O[dt] = mfma_bf16(a, bl, o);
+            }
+        }
+    };
+
     // ---- PV of one step: O^T += V^T (P * s_v)^T per group; the bias term of all
     //      groups in one MFMA.  Per-row visibility is carried by p (< 0: hidden);
     //      kin: key inside the item's range, so its slot holds data (A side, where
@@ -472,6 +533,13 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     auto pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8], auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
         if (sb_on) sm.vsb[wave][sb_g][sb_key] = vr.sb;
+        // fp16 operands hold p * s_v (p <= 2^8) and the V bias only while
+        // s_v < 2^7 and |bias| < 2^15; a visible key beyond that sends this
+        // wave's step down the bf16 path, whose operands have fp32 range.
+        const int vkey = st + sb_key;
+        const bool big = sb_on && vkey >= j0 && vkey < j1 &&
+                         ((vr.sb & 0x7FFFu) >= 0x4300u || ((vr.sb >> 16) & 0x7FFFu) >= 0x4700u);
+        const bool wide = __builtin_amdgcn_ballot_w64(big) != 0;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -482,6 +550,10 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             const int key = st + 8 * lg + k;
             kin[k] = FULL || (key >= j0 && key < j1);
             pp[k] = FULL ? p[k] : fmaxf(p[k], 0.0f);
+        }
+        if (wide) {
+            pv_wide(vr, p, pp, kin, FULL);
+            return;
         }
         {
             f16x8 pb, ac;

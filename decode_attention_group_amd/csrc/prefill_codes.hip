@@ -260,22 +260,37 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     };
 
     // ---- q of this lane's row as MFMA B operands, in the K element order
+    // The row enters the MFMA as fp16 after a power of 2 that puts its largest
+    // magnitude in [2^14, 2^15) (bf16 -> fp16 exact for every value within 2^-28
+    // of it, at any magnitude of q); the scores are multiplied back by qinv.
     f16x8 qf[KS];
+    float qinv;
     {
         const uint16_t* qrow = as_global(P.q[0]) + ((((int64_t)b * P.Hq + hq) * C + qi) * D);
+        u32x4 u[KS];
+        float amax = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 u = 0;
-            if (row_ok) u = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+            u[ks] = 0;
+            if (row_ok) u[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_lo_to_f32(u[ks][e])), fabsf(bf16_hi_to_f32(u[ks][e]))));
+        }
+        const uint32_t ex = min(max((__float_as_uint(max_across_groups(amax)) >> 23) & 0xFFu, 15u), 254u);
+        const float qmul = __uint_as_float((268u - ex) << 23);
+        qinv = __uint_as_float((ex - 14u) << 23);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
             float f[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { f[2 * e] = bf16_lo_to_f32(u[e]); f[2 * e + 1] = bf16_hi_to_f32(u[e]); }
+            for (int e = 0; e < 4; ++e) { f[2 * e] = bf16_lo_to_f32(u[ks][e]); f[2 * e + 1] = bf16_hi_to_f32(u[ks][e]); }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)f[KB == 8 ? e : nib_order(e)];
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(f[KB == 8 ? e : nib_order(e)] * qmul);
         }
     }
 
-    const float sl2e = P.scale_log2e;
+    const float sl2e = P.scale_log2e * qinv;
     f32x4 O[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};

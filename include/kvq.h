@@ -47,13 +47,18 @@
  *     (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
  *   - Precision: products accumulate in fp32 and out is rounded once to bf16.
  *     On quantized caches, decode reads, the decode step, shared and mixed
- *     reads, and chunks that take the split read multiply the codes exactly; q
- *     enters as fp16 (exact for 2^-14 <= |q| < 65504) and p * v_scale as fp16,
- *     so V scales must stay below 255.  Chunks of 17..64 query rows per KV head
- *     (rows = chunk * Hq/Hkv) with head_dim >= 256 over more than 2048 keys
- *     dequantize K and V to fp16 (2^-11 relative; |value| < 65504); chunks of
- *     more than 64 rows per KV head with head_dim >= 256 dequantize them to
- *     bf16 tiles (2^-9 relative), which moves a logit by up to
+ *     reads, and chunks of up to 16 query rows per KV head (rows = chunk *
+ *     Hq/Hkv) multiply the codes exactly and take any finite q and any cache
+ *     the append wrote: q enters the fp16 MFMAs after a power of 2 per row and
+ *     64-group (exact for every value within 2^-28 of the group's largest), and
+ *     a step whose V scales reach 2^7 or V biases 2^15 runs its value product on
+ *     bf16 operands split in two parts (about 16 bits) instead of fp16.  Chunks
+ *     of 17..64 rows per KV head with head_dim >= 256 over more than 2048 keys
+ *     normalize q per row the same way but dequantize K and V to fp16 (2^-11
+ *     relative), so their values and scales must stay below 2^15 in magnitude
+ *     (past that the output is not finite); chunks of more than 64 rows per KV
+ *     head with head_dim >= 256 dequantize K and V to bf16 tiles (2^-9
+ *     relative; any magnitude), which moves a logit by up to
  *     scale * 2^-9 * sum_i |q_i k_i|: negligible at scale 1.0 on RMS-normalised
  *     q and k, a few hundredths of an output when the logits spread over
  *     hundreds.  Reads of bf16 caches multiply the stored values exactly, with
