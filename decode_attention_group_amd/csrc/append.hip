@@ -105,8 +105,13 @@ hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream)
 {
     const dim3 grid(n_cand, p.H, 2 * p.B);
     switch (p.D) {
+    case 64: append_kernel<64><<<grid, 256, 0, stream>>>(p); break;
     case 128: append_kernel<128><<<grid, 256, 0, stream>>>(p); break;
+    case 192: append_kernel<192><<<grid, 256, 0, stream>>>(p); break;
     case 256: append_kernel<256><<<grid, 256, 0, stream>>>(p); break;
+    case 320: append_kernel<320><<<grid, 256, 0, stream>>>(p); break;
+    case 384: append_kernel<384><<<grid, 256, 0, stream>>>(p); break;
+    case 448: append_kernel<448><<<grid, 256, 0, stream>>>(p); break;
     case 512: append_kernel<512><<<grid, 256, 0, stream>>>(p); break;
     default: return hipErrorInvalidValue;
     }

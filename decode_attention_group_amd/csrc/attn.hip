@@ -39,9 +39,12 @@ namespace kvq {
 template <int D>
 struct Shape {
     static constexpr int G = D / 64;
-    static constexpr int NW = G >= 4 ? 4 : G;      // waves per workgroup
-    static constexpr int GPW = G / NW;              // groups per wave
+    // waves per workgroup: one per group up to four groups, else one per pair of
+    // groups (6, 8) or one per group (5, 7)
+    static constexpr int NW = G <= 4 ? G : (G % 2 == 0 ? G / 2 : G);
+    static constexpr int GPW = G / NW;              // groups per wave (1 or 2)
     static constexpr int DTW = 4 * GPW;             // 16-column tiles of O^T per wave
+    static_assert(G * 64 == D && G >= 1 && G <= 8 && NW * GPW == G, "head_dim a multiple of 64 up to 512");
 };
 
 template <int D>
@@ -119,9 +122,11 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
 {
     constexpr int NT = 64 * Shape<D>::NW;           // threads
     constexpr int G = D / 64, CH = D / 8, VW = VB / 4;
-    constexpr int PARTS = NT / kRowTile;            // lanes per query row in the dot product
+    // lanes per query row in the dot product: a power of 2 (shuffle reduction)
+    // that leaves each lane a multiple of 8 elements
+    constexpr int PARTS = NT / kRowTile >= 16 && G % 2 == 0 ? 16 : NT / kRowTile >= 8 ? 8 : NT / kRowTile;
     constexpr int EPP = D / PARTS;                  // elements per lane
-    static_assert(2 * CH <= NT && EPP % 8 == 0, "one chunk per thread");
+    static_assert(2 * CH <= NT && EPP % 8 == 0 && EPP * PARTS == D, "one chunk per thread");
     static_assert((2 * D * 4 + D) <= (int)sizeof(AttnSmem<D>), "fits the attention LDS");
     float* khat = lds;
     float* vhat = lds + D;
@@ -173,9 +178,9 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
         }
     }
     // q . khat for each row of the tile: PARTS consecutive lanes per row
-    const int r = tid / PARTS, part = tid % PARTS;
+    const int r = tid / PARTS, part = tid % PARTS;     // threads past 16 rows compute nothing used
     const int grow = rt * kRowTile + r;
-    const bool row_ok = grow < P.n_rows;
+    const bool row_ok = r < kRowTile && grow < P.n_rows;
     const RowMap rm = map_row(P, hkv, row_ok ? grow : rt * kRowTile);
     const uint16_t* qrow = as_global(P.q[0]) + ((((int64_t)b * P.Hq + rm.hq) * P.C + rm.qi) * D + part * EPP);
     const float* kh = khat + part * EPP;
@@ -733,14 +738,14 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
     const AttnDesc& d = P.d[di];
     const int idx = bid - d.item_begin;
     switch (d.cfg) {
-    case 4: attn_body<256, 4, 4>(d, idx, sm256); break;
-    case 5: attn_body<256, 4, 8>(d, idx, sm256); break;
-    case 6: attn_body<256, 8, 4>(d, idx, sm256); break;
-    case 7: attn_body<256, 8, 8>(d, idx, sm256); break;
-    case 8: attn_body<512, 4, 4>(d, idx, sm); break;
-    case 9: attn_body<512, 4, 8>(d, idx, sm); break;
-    case 10: attn_body<512, 8, 4>(d, idx, sm); break;
-    case 11: attn_body<512, 8, 8>(d, idx, sm); break;
+    case cfg_of(256, 4, 4): attn_body<256, 4, 4>(d, idx, sm256); break;
+    case cfg_of(256, 4, 8): attn_body<256, 4, 8>(d, idx, sm256); break;
+    case cfg_of(256, 8, 4): attn_body<256, 8, 4>(d, idx, sm256); break;
+    case cfg_of(256, 8, 8): attn_body<256, 8, 8>(d, idx, sm256); break;
+    case cfg_of(512, 4, 4): attn_body<512, 4, 4>(d, idx, sm); break;
+    case cfg_of(512, 4, 8): attn_body<512, 4, 8>(d, idx, sm); break;
+    case cfg_of(512, 8, 4): attn_body<512, 8, 4>(d, idx, sm); break;
+    case cfg_of(512, 8, 8): attn_body<512, 8, 8>(d, idx, sm); break;
     default: break;
     }
 }
@@ -849,13 +854,13 @@ hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStre
     }
     switch (p.d[0].cfg) {
 #define KVQ_CASE(D_, KB_, VB_) \
-    case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
+    case cfg_of(D_, KB_, VB_): \
         if (p.n_desc == 1) attn_kernel<D_, KB_, VB_, true><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
         else attn_kernel<D_, KB_, VB_, false><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
         break;
-    KVQ_CASE(128, 4, 4) KVQ_CASE(128, 4, 8) KVQ_CASE(128, 8, 4) KVQ_CASE(128, 8, 8)
-    KVQ_CASE(256, 4, 4) KVQ_CASE(256, 4, 8) KVQ_CASE(256, 8, 4) KVQ_CASE(256, 8, 8)
-    KVQ_CASE(512, 4, 4) KVQ_CASE(512, 4, 8) KVQ_CASE(512, 8, 4) KVQ_CASE(512, 8, 8)
+#define KVQ_D(D_) KVQ_CASE(D_, 4, 4) KVQ_CASE(D_, 4, 8) KVQ_CASE(D_, 8, 4) KVQ_CASE(D_, 8, 8)
+    KVQ_D(64) KVQ_D(128) KVQ_D(192) KVQ_D(256) KVQ_D(320) KVQ_D(384) KVQ_D(448) KVQ_D(512)
+#undef KVQ_D
 #undef KVQ_CASE
     default: return hipErrorInvalidValue;
     }

@@ -72,8 +72,11 @@ kvq_status check_cache(const kvq_cache* c, const char* what)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: a cache array pointer is NULL", what);
     if (c->group_size != KVQ_GROUP_SIZE)
         return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (only 64 is supported)", what, c->group_size);
-    if (c->head_dim != 128 && c->head_dim != 256 && c->head_dim != 512)
-        return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256, 512)", what, c->head_dim);
+    if (c->head_dim < 64 || c->head_dim > 512 || c->head_dim % 64 != 0)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: multiples of 64 up to 512)", what, c->head_dim);
+    if (bf16 && c->head_dim % 128 != 0)
+        return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d on a bf16 cache (supported: 128, 256, 384, 512)", what,
+                    c->head_dim);
     if (!bf16 && ((c->k_bits != 4 && c->k_bits != 8) || (c->v_bits != 4 && c->v_bits != 8)))
         return fail(KVQ_ERR_UNSUPPORTED, "%s: k_bits %d / v_bits %d (each 4 or 8, or both 16)", what, c->k_bits,
                     c->v_bits);
@@ -289,7 +292,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     bool same = true, big = true;
     for (int i = 0; i < n; ++i) {
         same &= P.d[i].cfg == P.d[0].cfg;
-        big &= P.d[i].D >= 256 && !kvq::cfg_is_bf16(P.d[i].cfg);
+        big &= kvq::chunk_kernels_for(P.d[i].D) && !kvq::cfg_is_bf16(P.d[i].cfg);
     }
     auto launch_one = [&](const kvq::AttnParams& p, int items) {
         return kvq::cfg_is_bf16(p.d[0].cfg) ? kvq::launch_attn_bf16(p, items, stream)
@@ -470,7 +473,7 @@ enum class ChunkPath { kDecode, kCodes, kBand };
 
 ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
 {
-    const bool big = chunk > 1 && c->head_dim >= 256;
+    const bool big = chunk > 1 && kvq::chunk_kernels_for(c->head_dim);
     if (c->k_bits == 16) {                 // bf16 caches: the bf16 split kernel, or the band (no short-chunk kernel)
         const char* f = getenv("KVQ_PREFILL_PATH");
         if (f && *f) return big && f[0] == 'b' ? ChunkPath::kBand : ChunkPath::kDecode;

@@ -64,15 +64,17 @@ struct AttnParams {
     int32_t n_desc;
 };
 
-// Configuration id: 0..11 quantized (head_dim, k_bits, v_bits); 12..14 bf16
-// caches (head_dim 128, 256, 512).
-inline int cfg_id(int D, int kb, int vb)
+// Configuration id: 0..31 quantized (head_dim 64..512 in steps of 64, k_bits,
+// v_bits); 32 + head_dim/64 - 1 for bf16 caches.
+constexpr int cfg_of(int D, int kb, int vb)
 {
-    const int di = D == 128 ? 0 : D == 256 ? 1 : 2;
-    if (kb == 16) return 12 + di;
-    return di * 4 + (kb == 8 ? 2 : 0) + (vb == 8 ? 1 : 0);
+    return kb == 16 ? 32 + D / 64 - 1 : (D / 64 - 1) * 4 + (kb == 8 ? 2 : 0) + (vb == 8 ? 1 : 0);
 }
-inline bool cfg_is_bf16(int cfg) { return cfg >= 12; }
+inline int cfg_id(int D, int kb, int vb) { return cfg_of(D, kb, vb); }
+inline bool cfg_is_bf16(int cfg) { return cfg >= 32; }
+// The chunk kernels (band and short-chunk) and the two-configuration decode
+// launch exist for the model's head_dims; every other read takes the decode kernel.
+inline bool chunk_kernels_for(int D) { return D == 256 || D == 512; }
 
 // Partial buffer of one descriptor: o [B*Hkv*n_rt][S][16][D] fp32, then
 // (m, l) [B*Hkv*n_rt][S][16][2] fp32.

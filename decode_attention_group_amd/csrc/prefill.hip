@@ -657,14 +657,14 @@ hipError_t launch_band(const AttnParams& p, hipStream_t stream)
     const dim3 dq_grid(d.nk / kStep, d.Hkv, d.B), block(256);
     switch (d.cfg) {
 #define KVQ_DQ(D_, KB_, VB_) \
-    case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
+    case cfg_of(D_, KB_, VB_): \
         band_dequant_kernel<D_, KB_, VB_><<<dq_grid, block, 0, stream>>>(d); break;
     KVQ_DQ(256, 4, 4) KVQ_DQ(256, 4, 8) KVQ_DQ(256, 8, 4) KVQ_DQ(256, 8, 8)
     KVQ_DQ(512, 4, 4) KVQ_DQ(512, 4, 8) KVQ_DQ(512, 8, 4) KVQ_DQ(512, 8, 8)
 #undef KVQ_DQ
-    case 13: case 14:      // bf16 caches: the attention kernel reads the cache itself (no band)
+    case cfg_of(256, 16, 16): case cfg_of(512, 16, 16):   // bf16: the attention kernel reads the cache itself
         if (d.band != nullptr) {
-            if (d.cfg == 13) band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d);
+            if (d.cfg == cfg_of(256, 16, 16)) band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d);
             else band_bf16_kernel<512><<<dq_grid, block, 0, stream>>>(d);
         }
         break;

@@ -431,7 +431,7 @@ hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_
     const dim3 grid(total_items);
     switch (p.d[0].cfg) {
 #define KVQ_CP(D_, KB_, VB_) \
-    case (D_ == 128 ? 0 : D_ == 256 ? 1 : 2) * 4 + (KB_ == 8 ? 2 : 0) + (VB_ == 8 ? 1 : 0): \
+    case cfg_of(D_, KB_, VB_): \
         codes_prefill_kernel<D_, KB_, VB_><<<grid, dim3(CpShape<D_>::NT), 0, stream>>>(p); break;
     KVQ_CP(256, 4, 4) KVQ_CP(256, 4, 8) KVQ_CP(256, 8, 4) KVQ_CP(256, 8, 8)
     KVQ_CP(512, 4, 4) KVQ_CP(512, 4, 8) KVQ_CP(512, 8, 4) KVQ_CP(512, 8, 8)

@@ -53,11 +53,11 @@
  *     64-group (exact for every value within 2^-28 of the group's largest), and
  *     a step whose V scales reach 2^7 or V biases 2^15 runs its value product on
  *     bf16 operands split in two parts (about 16 bits) instead of fp16.  Chunks
- *     of 17..64 rows per KV head with head_dim >= 256 over more than 2048 keys
+ *     of 17..64 rows per KV head with head_dim 256 or 512 over more than 2048 keys
  *     normalize q per row the same way but dequantize K and V to fp16 (2^-11
  *     relative), so their values and scales must stay below 2^15 in magnitude
  *     (past that the output is not finite); chunks of more than 64 rows per KV
- *     head with head_dim >= 256 dequantize K and V to bf16 tiles (2^-9
+ *     head with head_dim 256 or 512 dequantize K and V to bf16 tiles (2^-9
  *     relative; any magnitude), which moves a logit by up to
  *     scale * 2^-9 * sum_i |q_i k_i|: negligible at scale 1.0 on RMS-normalised
  *     q and k, a few hundredths of an output when the logits spread over
@@ -78,7 +78,7 @@ extern "C" {
 typedef enum {
     KVQ_OK = 0,
     KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad count, Hq % Hkv != 0, ...      */
-    KVQ_ERR_UNSUPPORTED = 2,      /* bits not 4/8 (or both 16), group != 64, head_dim not 128/256/512 */
+    KVQ_ERR_UNSUPPORTED = 2,      /* bits not 4/8 (or both 16), group != 64, head_dim not k*64 <= 512 */
     KVQ_ERR_CAPACITY = 3,         /* window > capacity, cache cannot hold the visible keys */
     KVQ_ERR_WORKSPACE = 4,        /* workspace smaller than the *_workspace_bytes query  */
     KVQ_ERR_HIP = 5               /* a HIP launch error                                   */
@@ -122,9 +122,12 @@ typedef enum {
  * not used and may be NULL.  Every call takes such a cache; kvq_decode_step
  * rounds the step's token to bf16 where it would quantize it.
  *
- * Requirements: group_size == 64; head_dim in {128, 256, 512}; k_bits, v_bits in
- * {4, 8}, or both 16; capacity a multiple of 8 and at least KVQ_MIN_CAPACITY;
- * 0 <= window <= capacity (0: full).
+ * Requirements: group_size == 64; head_dim a multiple of 64 from 64 to 512 (a bf16
+ * cache: a multiple of 128); k_bits, v_bits in {4, 8}, or both 16; capacity a
+ * multiple of 8 and at least KVQ_MIN_CAPACITY; 0 <= window <= capacity (0: full).
+ * Chunk reads of more than 16 rows per KV head have kernels of their own at
+ * head_dim 256 and 512 (the model's); at the other head_dims every read runs on
+ * the decode kernel, which reads the keys once per 16-row tile.
  */
 typedef struct {
     uint32_t *k_codes;

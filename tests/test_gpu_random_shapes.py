@@ -1,7 +1,7 @@
 """Seeded random shapes through every read against the fp64 oracle.
 
-Each case draws, from its own seed: head_dim (128/256/512), K and V widths
-(4 or 8 each, or a bf16 cache), KV heads and query heads per KV head, batch,
+Each case draws, from its own seed: head_dim (any multiple of 64 up to 512;
+a bf16 cache a multiple of 128), K and V widths (4 or 8 each, or a bf16 cache), KV heads and query heads per KV head, batch,
 window (full or a random width) and ring capacity (a multiple of 8, at least
 32, large enough for the read), a length, and the call: decode, fused decode
 step, or a chunk of 2..80 queries.  The GPU appends its own cache (codes
@@ -19,13 +19,13 @@ from test_gpu_attention import q_dev
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 128
 
 
 def draw(seed):
     rng = np.random.default_rng(1000 + seed)
-    D = int(rng.choice([128, 256, 512]))
-    if rng.random() < 0.2:
+    D = int(rng.choice([64, 128, 192, 256, 320, 384, 448, 512]))
+    if rng.random() < 0.2 and D % 128 == 0:
         kb = vb = 16
     else:
         kb, vb = int(rng.choice([4, 8])), int(rng.choice([4, 8]))
@@ -83,3 +83,33 @@ def test_random_shape(seed):
         ref = o.attend(qb, lens)
     assert_cache_equal(g, o)              # codes (or bf16 values) written by the GPU, bit for bit
     assert_close(torch_bf16_to_f64(out), ref, f"random case {seed} {c}")
+
+
+@pytest.mark.parametrize("dims", [(64, 192), (320, 448), (384, 256)])
+def test_shared_launch_mixed_head_dims(dims):
+    """One shared call over two caches of other head_dims (two layers on the first,
+    one on the second), each layer against the oracle."""
+    B, L = 2, 900
+    groups, refs = [], []
+    lens = np.full(B, L, np.int32)
+    lens_d = torch.from_numpy(lens).cuda()
+    for i, D in enumerate(dims):
+        H, W = (2, 256) if i == 0 else (1, 0)
+        R = W + 8 if W else (L + 7) // 8 * 8
+        kb, vb = (4, 8) if i == 0 else (8, 4)
+        k = small_randn(5000 + D, (B, H, L, D), D ** -0.25)
+        v = small_randn(5001 + D, (B, H, L, D), D ** -0.25)
+        g = kvq.KVCache(B, H, D, kb, vb, R, window=W)
+        o = oracle.Cache(B, H, D, R, kb, vb, window=W)
+        kvq.kvq_append_quantize(g, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                                torch.zeros(B, dtype=torch.int32, device="cuda"))
+        o.append(k, v, np.zeros(B, np.int32))
+        qs = [small_q_bits(5002 + D + j, (B, 4 * H, 1, D), D ** -0.25) for j in range(2 - i)]
+        groups.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens_d, L))
+        refs.append([o.attend(x, lens)[:, :, 0] for x in qs])
+    print(f"shared head_dims {dims}", flush=True)
+    outs = kvq.kvq_attn_decode_shared(groups)
+    torch.cuda.synchronize()
+    for res, ref in zip(outs, refs):
+        for out, r in zip(res, ref):
+            assert_close(torch_bf16_to_f64(out), r, f"shared {dims}")
