@@ -288,6 +288,8 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     const size_t need = plan_all(rs, n, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
     bind_workspace(P, workspace);
     bool same = true, big = true;
     for (int i = 0; i < n; ++i) {
@@ -683,6 +685,8 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     const size_t need = path == ChunkPath::kBand ? plan_prefill(r, P, total_items) : plan_codes(r, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
     if (path == ChunkPath::kCodes) {
         P.d[0].part = kvq::part_floats(P.d[0]) ? static_cast<float*>(workspace) : nullptr;
         if (trace_on())

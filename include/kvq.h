@@ -43,8 +43,8 @@
  *     unspecified, though every memory access stays inside the cache.
  *   - Calls that share one cache, workspace or output on one device must be
  *     ordered (same stream or events); concurrent calls on such buffers race.
- *   - Alignment: cache arrays, k and v 16 bytes; q 16 bytes; out 8 bytes
- *     (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
+ *   - Alignment: cache arrays, k and v 16 bytes; q 16 bytes; out 8 bytes; a
+ *     workspace 16 bytes (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
  *   - Precision: products accumulate in fp32 and out is rounded once to bf16.
  *     On quantized caches, decode reads, the decode step, shared and mixed
  *     reads, and chunks of up to 16 query rows per KV head (rows = chunk *

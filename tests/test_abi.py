@@ -65,8 +65,8 @@ def cache(**kw):
     return kvq.CacheStruct(**c)
 
 
-def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAKE):
-    return lib.kvq_attn_decode(ctypes.byref(c), q, Hq, ln, max_len, scale, out, None, ws, None)
+def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAKE, ws_ptr=None):
+    return lib.kvq_attn_decode(ctypes.byref(c), q, Hq, ln, max_len, scale, out, ws_ptr, ws, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -98,6 +98,17 @@ def test_decode_argument_validation(lib):
     big = cache(window=0, capacity=32768, head_dim=512, n_kv_heads=1, k_bits=8, v_bits=8, batch=4)
     assert decode(lib, big, max_len=32768, ws=0) == 4  # split partials need a workspace
     assert "workspace" in lib.kvq_last_error().decode()
+    assert decode(lib, big, max_len=32768, ws=1 << 30, ws_ptr=FAKE + 8) == 1   # misaligned workspace
+    assert "16-byte" in lib.kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("C", [8, 512])
+def test_prefill_workspace_alignment(lib, C):
+    """The short-chunk (8 queries: 64 rows over 32768 keys) and band (512 queries)
+    paths refuse a workspace that is not 16-byte aligned, before any launch."""
+    c = cache(window=0, capacity=32768, head_dim=512, n_kv_heads=1, k_bits=8, v_bits=8, batch=4)
+    st = lib.kvq_attn_prefill_chunk(ctypes.byref(c), FAKE, 8, C, FAKE, 32768, 1.0, FAKE, FAKE + 4, 1 << 34, None)
+    assert st == 1 and "16-byte" in lib.kvq_last_error().decode()
 
 
 def test_prefill_validation(lib):
