@@ -288,7 +288,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     const size_t need = plan_all(rs, n, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
     bind_workspace(P, workspace);
     bool same = true, big = true;
@@ -545,6 +545,36 @@ size_t plan_prefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
     return part + (size_t)d.B * d.Hkv * (d.nk + 4 * kvq::kStep) * d.D * 2 * sizeof(uint16_t);
 }
 
+// Quantized caches, chunks of more than 64 rows per KV head (head_dim 256/512):
+// one workgroup per (b, kv head, 32-row block, split) of the fused kernel, which
+// reads the codes itself; the workspace holds the split partials only.
+size_t plan_qprefill(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
+{
+    std::memset(&P, 0, sizeof(P));
+    P.n_desc = 1;
+    plan_read(r, 1, P.d[0]);                      // shape fields (n_rt counts 16-row tiles)
+    kvq::AttnDesc& d = P.d[0];
+    const kvq_cache* c = r.cache;
+    const int n_rb = (d.n_rows + kvq::kQprefillRows - 1) / kvq::kQprefillRows;
+    int64_t vis = r.max_len;
+    if (c->window > 0)
+        vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kQprefillRows + d.hpk - 1) / d.hpk);
+    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
+    const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
+    // one workgroup per CU (each holds a wave per SIMD); split keys only below that
+    const int kTargetWg = 256;
+    int64_t S = (kTargetWg + items - 1) / items;
+    const int forced = env_splits();
+    if (forced > 0) S = forced;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>((steps + 3) / 4, kvq::kMaxSplits)));
+    const int64_t steps_per = (steps + S - 1) / S;
+    d.split_len = (int)(steps_per * kvq::kStep);
+    d.S = (int)((steps + steps_per - 1) / steps_per);
+    d.n_items = (int)(items * d.S);
+    total_items = d.n_items;
+    return kvq::part_floats(d) * sizeof(float);
+}
+
 // Short-chunk kernel: one workgroup per (b, kv head, 64-row block, split); the
 // workspace holds the split partials only.
 size_t plan_codes(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
@@ -591,7 +621,8 @@ KVQ_API size_t kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_q_h
     kvq::AttnParams P;
     int total = 0;
     switch (chunk_path(cache, n_q_heads, chunk, max_len)) {
-    case ChunkPath::kBand: return plan_prefill(r, P, total);
+    case ChunkPath::kBand: return kvq::cfg_is_bf16(kvq::cfg_id(cache->head_dim, cache->k_bits, cache->v_bits))
+                                      ? plan_prefill(r, P, total) : plan_qprefill(r, P, total);
     case ChunkPath::kCodes: return plan_codes(r, P, total);
     default: return plan_all(&r, 1, P, total);
     }
@@ -682,11 +713,26 @@ KVQ_API kvq_status kvq_attn_prefill_chunk(const kvq_cache* cache, const uint16_t
     if (path == ChunkPath::kDecode) return run_reads(&r, 1, workspace, workspace_bytes, stream, what);
     kvq::AttnParams P;
     int total_items = 0;
-    const size_t need = path == ChunkPath::kBand ? plan_prefill(r, P, total_items) : plan_codes(r, P, total_items);
+    const bool quant_band = path == ChunkPath::kBand && cache->k_bits != 16;
+    const size_t need = quant_band ? plan_qprefill(r, P, total_items)
+                        : path == ChunkPath::kBand ? plan_prefill(r, P, total_items) : plan_codes(r, P, total_items);
     if (workspace_bytes < need || (need > 0 && !workspace))
         return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", what, workspace_bytes, need);
-    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
+    if (quant_band) {
+        P.d[0].part = kvq::part_floats(P.d[0]) ? static_cast<float*>(workspace) : nullptr;
+        if (trace_on())
+            fprintf(stderr, "[kvq] %s quantized prefill kernel: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d S=%d "
+                    "split=%d wg=%d\n", what, P.d[0].B, P.d[0].Hkv, P.d[0].Hq, P.d[0].D, P.d[0].R, P.d[0].W,
+                    P.d[0].C, P.d[0].n_rows, P.d[0].S, P.d[0].split_len, total_items);
+        mark_before(stream);
+        hipError_t e = kvq::launch_qprefill(P, total_items, stream);
+        mark_after(stream);
+        if (e == hipSuccess) e = kvq::launch_combine(P, stream);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+        return ok();
+    }
     if (path == ChunkPath::kCodes) {
         P.d[0].part = kvq::part_floats(P.d[0]) ? static_cast<float*>(workspace) : nullptr;
         if (trace_on())

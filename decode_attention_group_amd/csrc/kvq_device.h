@@ -27,6 +27,17 @@ __device__ __forceinline__ T* as_global(T* p)
     return (T*)reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Work item of workgroup `bid` of `n`: workgroups are dealt to the 8 XCDs in
+// turn, so this gives each XCD a run of consecutive items (items that read the
+// same keys then share that XCD's L2).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int bid, int n)
+{
+    const int x = bid % kXcds, k = bid / kXcds;
+    const int q = n / kXcds, r = n % kXcds;
+    return x * q + min(x, r) + k;
+}
+
 // Slot of a position already reduced to [0, 2R): one conditional subtraction.
 __device__ __forceinline__ int wrap_slot(int slot, int R) { return slot >= R ? slot - R : slot; }
 

@@ -95,6 +95,9 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 hipError_t launch_band(const AttnParams& p, hipStream_t stream);
 hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_t stream);
+// Chunks over quantized caches: the fused kernel (32-row items, codes read in place).
+hipError_t launch_qprefill(const AttnParams& p, int total_items, hipStream_t stream);
+constexpr int kQprefillRows = 32;
 
 // Query rows per prefill workgroup (two 16-row tiles).
 constexpr int kPrefillRows = 32;

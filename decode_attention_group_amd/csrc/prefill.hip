@@ -1,36 +1,29 @@
-// Chunked-prefill attention over an affine group-quantized cache, gfx950.
+// Chunked-prefill attention over an unquantized bf16 cache (the pages' bf16
+// sliding layers), gfx950.  Quantized caches have their own prefill kernel
+// (prefill_q.hip), which reads the codes in place.
 //
 // What it computes (page 80 of the @mlx-bun/inference 0.0.0-stage -> 1.0.0
 // diff, gemma4/model.ts: a prompt chunk's tokens are appended to the cache and
 // its queries then attend the cache read -- causal inside the chunk, windowed
 // on sliding layers): for query i of a chunk of C, at position p = len - C + i,
-// softmax(scale * q . khat_j) over max(0, p-W+1, len-R) <= j <= p, times vhat_j.
+// softmax(scale * q . k_j) over max(0, p-W+1, len-R) <= j <= p, times v_j.
 //
-// Unlike decode, every key of the chunk's band is read by many query rows (the
-// chunk's queries times the query heads of its KV head), so it is dequantized
-// once per call and the attention itself is a plain bf16 flash attention:
-//   band_dequant_kernel: for each (sequence, KV head), the positions any query
-//     of the chunk can see -- the band [base0, len), base0 = that lowest
-//     position rounded down to 32 -- dequantized x = code * scale + bias in
-//     fp32, rounded to bf16, into the workspace as one tile per 32-key step,
-//     laid out exactly as the attention kernel wants it in LDS: the step's 32 K
-//     rows (in MFMA row order) and then its D V^T rows (keys contiguous per
-//     element), 16-byte chunks XOR-swizzled so the MFMA operand reads hit
-//     distinct banks.  Band positions outside what the chunk can see are zeros.
 //   prefill_kernel: one workgroup per (sequence, KV head, 32 query rows,
-//     split).  Tiles are copied global -> LDS with LDS DMA (no register
-//     staging) one round ahead of their use.  Each wave owns RT row tiles of
-//     16 rows, so every K / V^T operand read from LDS feeds RT MFMAs (LDS
-//     bandwidth bounds the one-tile-per-wave layout); the NG wave groups take
-//     alternate steps and merge in LDS at the end.  S^T = K Q^T and
-//     O^T = V^T P^T run on 16x16x32 bf16 MFMA with an online softmax in base 2
-//     (lazy rescale: the running max may trail the true one by up to 2^8).
-// An unquantized bf16 cache needs no dequantization: the attention kernel then
-// DMAs each step's tiles straight from the cache (every lane addressing its own
-// 16-byte chunk, the same LDS image), and zeroes the V^T entries of positions
-// outside the band, which a ring slot or a never-written slot may fill with
-// anything.  band_bf16_kernel (the band as a copy) remains for caches too large
-// for 32-bit DMA offsets.
+//     split).  Each 32-key step's tiles -- its 32 K rows (in MFMA row order),
+//     then its D V^T rows (keys contiguous per element), 16-byte chunks
+//     XOR-swizzled so the MFMA operand reads hit distinct banks -- are copied
+//     global -> LDS with LDS DMA (no register staging) one round ahead of
+//     their use, every lane addressing its own 16-byte chunk of the cache, and
+//     the V^T entries of positions outside the band [base0, len) (base0 = the
+//     lowest position any query of the chunk sees, rounded down to 32), which a
+//     ring slot or a never-written slot may fill with anything, are zeroed.
+//     Each wave owns RT row tiles of 16 rows, so every K / V^T operand read
+//     from LDS feeds RT MFMAs; the NG wave groups take alternate steps and
+//     merge in LDS at the end.  S^T = K Q^T and O^T = V^T P^T run on 16x16x32
+//     bf16 MFMA with an online softmax in base 2 (lazy rescale: the running
+//     max may trail the true one by up to 2^8).
+//   band_bf16_kernel: the same tiles as a copy in the workspace, for caches
+//     too large for the DMA's 32-bit offsets; prefill_kernel then reads them.
 // Rows follow the decode layout (row = query * (Hq/Hkv) + head), so split
 // partials, if any, go through the same combine kernel.
 #include <type_traits>
@@ -79,118 +72,11 @@ template <int D>
 __device__ __forceinline__ int v_chunk_pos(int d, int c) { return 4 * D + d * 4 + (c ^ ((d >> 2) & 3)); }
 
 // ---------------------------------------------------------------------------
-// Band dequantization.  Grid (band steps, Hkv, B), 256 threads; one 32-key
-// step per workgroup.  K: thread -> (key tid/8, D/8 elements); V: thread ->
-// element d (and d + 256), 32 keys.
-template <int D, int KB, int VB>
-__global__ __launch_bounds__(256) void band_dequant_kernel(AttnDesc P)
-{
-    constexpr int G = D / 64;
-    constexpr int KW = D * KB / 32;          // K code words per slot
-    constexpr int VW = VB / 4;               // V code words per (block, d)
-    constexpr int KE = D / 8;                // K elements per thread
-    __shared__ uint32_t vsb[kStep][G];       // V scale|bias words of the step
-    static_assert(kStep * G <= 256, "one V scale|bias word per thread");
-    const int tid = threadIdx.x;
-    const int step = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-    const int bh = b * P.Hkv + hkv;
-    const int R = P.R;
-    const int64_t kslot0 = (int64_t)bh * R;
-    const int key = tid >> 3, ch = tid & 7;              // K: key tid/8, elements [KE*(tid%8), +KE)
-    constexpr int KWT = KE * KB / 32;                     // K code words per thread
-    constexpr int VD = (D + 255) / 256;                   // elements d per thread
-
-    // len[b] (a vector load, waited for only where it is used) arrives while
-    // the codes are requested for len = max_len, the common case; another len
-    // requests them again.  Every load is issued before any store (stores in
-    // between would order the loads behind them).
-    int oz;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(oz));
-    const int len_lane = as_global(P.len)[b + oz];
-    int len, vis_lo, p0;
-    uint32_t vsbw, kw[KWT], ksbw, vw[VD][4][VW];
-    auto issue = [&](int l) {
-        len = l;
-        vis_lo = band_lo(len, P.C, P.W, R);
-        p0 = (vis_lo & ~(kStep - 1)) + step * kStep;
-        vsbw = tid < kStep * G ? as_global(P.v_sb)[(kslot0 + (p0 + tid / G) % R) * G + tid % G] : 0u;
-        const int64_t kslot = kslot0 + (p0 + key) % R;
-        const uint32_t* src = as_global(P.k_codes) + kslot * KW + ch * KWT;
-#pragma unroll
-        for (int w = 0; w < KWT; w += 4) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(src + w);
-            kw[w] = x.x; kw[w + 1] = x.y; kw[w + 2] = x.z; kw[w + 3] = x.w;
-        }
-        ksbw = as_global(P.k_sb)[kslot * G + ch * KE / 64];
-#pragma unroll
-        for (int dd = 0; dd < VD; ++dd)
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const int slot8 = (p0 + 8 * blk) % R;            // a multiple of 8
-                const uint32_t* vsrc = as_global(P.v_codes) + (((int64_t)bh * (R / 8) + slot8 / 8) * D + tid + 256 * dd) * VW;
-#pragma unroll
-                for (int w = 0; w < VW; ++w) vw[dd][blk][w] = vsrc[w];
-            }
-    };
-    issue(P.max_len);
-    const int len_act = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
-    if (len_act != len) issue(len_act);
-    if (p0 >= len) return;                   // past every query: never read
-    if (tid < kStep * G) vsb[tid / G][tid % G] = vsbw;
-    const int kpos = p0 + key;
-    const bool kok = kpos >= vis_lo && kpos < len;
-
-    {   // K
-        const float sc = bf16_lo_to_f32(ksbw), bi = bf16_hi_to_f32(ksbw);
-        uint16_t* tile = as_global(P.band) + ((int64_t)bh * (P.nk / kStep + kBandPad) + step) * tile_elems<D>();
-        const int row = k_row(key);
-#pragma unroll
-        for (int e0 = 0; e0 < KE; e0 += 8) {              // 8 elements: one 16-byte chunk
-            uint16_t* dst = tile + 8 * k_chunk_pos<D>(row, (ch * KE + e0) / 8);
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ei = e0 + e;
-                const uint32_t c = KB == 8 ? (kw[ei >> 2] >> (8 * (ei & 3))) & 0xFFu : (kw[ei >> 3] >> (4 * (ei & 7))) & 0xFu;
-                x[e] = kok ? __builtin_fmaf((float)c, sc, bi) : 0.0f;
-            }
-            const u32x4 o = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3]),
-                             bf16x2_rne(x[4], x[5]), bf16x2_rne(x[6], x[7])};
-            *reinterpret_cast<u32x4*>(dst) = o;
-        }
-    }
-    __syncthreads();
-    // V: element d, the step's 32 keys (4 blocks of 8 slots)
-#pragma unroll
-    for (int dd = 0; dd < VD; ++dd) {
-        const int d = tid + 256 * dd;
-        const int g = d / 64;
-        uint16_t* tile = as_global(P.band) + ((int64_t)bh * (P.nk / kStep + kBandPad) + step) * tile_elems<D>();
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            uint16_t* dst = tile + 8 * v_chunk_pos<D>(d, blk);
-            float x[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int k2 = 8 * blk + t, pos = p0 + k2;
-                const uint32_t c = VB == 8 ? (vw[dd][blk][t >> 2] >> (8 * (t & 3))) & 0xFFu : (vw[dd][blk][0] >> (4 * t)) & 0xFu;
-                const uint32_t sbw = vsb[k2][g];
-                x[t] = pos >= vis_lo && pos < len
-                           ? __builtin_fmaf((float)c, bf16_lo_to_f32(sbw), bf16_hi_to_f32(sbw)) : 0.0f;
-            }
-            const u32x4 o = {bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3]),
-                             bf16x2_rne(x[4], x[5]), bf16x2_rne(x[6], x[7])};
-            *reinterpret_cast<u32x4*>(dst) = o;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Band of an unquantized bf16 cache (page 80, gemma4/model.ts, note on
-// cacheLayers: sliding layers stay bf16 under the other KV scheme): the same
-// tiles as band_dequant_kernel, copied from the stored bf16 values with no
-// arithmetic (a K row's words are already pairs in element order, a V block's
-// 16 bytes the 8 keys of one element).  Grid and thread mapping as above.
+// cacheLayers: sliding layers stay bf16 under the other KV scheme): the tile
+// image above, copied from the stored bf16 values with no arithmetic (a K row's
+// words are already pairs in element order, a V block's 16 bytes the 8 keys of
+// one element).  Grid (band steps, Hkv, B), 256 threads.
 template <int D>
 __global__ __launch_bounds__(256) void band_bf16_kernel(AttnDesc P)
 {
@@ -240,7 +126,7 @@ __global__ __launch_bounds__(256) void band_bf16_kernel(AttnDesc P)
 }
 
 // ---------------------------------------------------------------------------
-// Attention over the dequantized band.
+// Attention over the band tiles (read in place from a bf16 cache, or copied).
 //
 // A workgroup covers 32 query rows (two row tiles: the 8192 rows of a 512-query
 // chunk fill 256 workgroups, one per CU).  Each wave owns RT row tiles of 16
@@ -636,13 +522,6 @@ __device__ __forceinline__ void prefill_body(const AttnDesc& P, int idx, PfSmem<
 // (the row blocks of one sequence and KV head, which all read the same band)
 // are given to one XCD, so the band is fetched into that XCD's L2 once and the
 // other row blocks hit it there.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_item(int bid, int n)
-{
-    const int x = bid % kXcds, k = bid / kXcds;
-    const int q = n / kXcds, r = n % kXcds;
-    return x * q + min(x, r) + k;
-}
 
 template <int D, bool DIRECT>
 __global__ __launch_bounds__(64 * pf_waves<D>()) void prefill_kernel(AttnParams P)
@@ -656,12 +535,6 @@ hipError_t launch_band(const AttnParams& p, hipStream_t stream)
     const AttnDesc& d = p.d[0];
     const dim3 dq_grid(d.nk / kStep, d.Hkv, d.B), block(256);
     switch (d.cfg) {
-#define KVQ_DQ(D_, KB_, VB_) \
-    case cfg_of(D_, KB_, VB_): \
-        band_dequant_kernel<D_, KB_, VB_><<<dq_grid, block, 0, stream>>>(d); break;
-    KVQ_DQ(256, 4, 4) KVQ_DQ(256, 4, 8) KVQ_DQ(256, 8, 4) KVQ_DQ(256, 8, 8)
-    KVQ_DQ(512, 4, 4) KVQ_DQ(512, 4, 8) KVQ_DQ(512, 8, 4) KVQ_DQ(512, 8, 8)
-#undef KVQ_DQ
     case cfg_of(256, 16, 16): case cfg_of(512, 16, 16):   // bf16: the attention kernel reads the cache itself
         if (d.band != nullptr) {
             if (d.cfg == cfg_of(256, 16, 16)) band_bf16_kernel<256><<<dq_grid, block, 0, stream>>>(d);

@@ -57,12 +57,12 @@
  *     normalize q per row the same way but dequantize K and V to fp16 (2^-11
  *     relative), so their values and scales must stay below 2^15 in magnitude
  *     (past that the output is not finite); chunks of more than 64 rows per KV
- *     head with head_dim 256 or 512 dequantize K and V to bf16 tiles (2^-9
- *     relative; any magnitude), which moves a logit by up to
- *     scale * 2^-9 * sum_i |q_i k_i|: negligible at scale 1.0 on RMS-normalised
- *     q and k, a few hundredths of an output when the logits spread over
- *     hundreds.  Reads of bf16 caches multiply the stored values exactly, with
- *     q as bf16 and the softmax weights rounded to bf16 for the value product.
+ *     head with head_dim 256 or 512 multiply the K codes exactly (q per row and
+ *     128-column slice, the K scale and bias in fp32 and bf16 parts, as the
+ *     decode read) and the V codes against p * v_scale in fp16, so their V
+ *     scales must stay below 2^7 and V biases below 2^15 in magnitude.  Reads of
+ *     bf16 caches multiply the stored values exactly, with q as bf16 and the
+ *     softmax weights rounded to bf16 for the value product.
  */
 #ifndef KVQ_H
 #define KVQ_H

@@ -6,10 +6,7 @@
   * identical keys: equal logits, the mean of the visible values;
   * a window of 1: each query sees only its own key;
   * a window of 1 on a chunk (3 and 100 queries): every row sees only itself;
-  * the large scale on chunks of 8 and 96 queries (every chunk path; the band
-    path against the oracle over bf16-rounded dequantized values, which is what
-    that path multiplies, at the attention tolerance, and against the exact
-    oracle within the bound that bf16 rounding of K and V allows).
+  * the large scale on chunks of 8 and 96 queries (every chunk path).
 Each on 4/8-bit and bf16 caches; outputs within the attention tolerance of the
 fp64 oracle (max-abs 1e-2, mean-abs 1e-3)."""
 import numpy as np
@@ -39,14 +36,6 @@ def build(B, H, D, kb, vb, R, W, k, v):
         o.append(k[:, :, t0:t1], v[:, :, t0:t1], pos0)
     return g, o
 
-
-def bf16_tile_oracle(o):
-    """The cache as the band path reads it: every dequantized value rounded to the
-    nearest bf16 (the path dequantizes K and V into bf16 tiles before its bf16
-    MFMAs).  Slot t of the ring keeps slot t's values."""
-    t = oracle.Cache(o.B, o.H, o.D, o.R, 16, 16, window=o.window)
-    t.append(o.dequant_k().astype(np.float32), o.dequant_v().astype(np.float32), np.zeros(o.B, np.int32))
-    return t
 
 
 def decode_check(g, o, q_bits, L, scale, what):
@@ -87,49 +76,14 @@ def test_large_scale_moves_the_running_max(bits, window):
     decode_check(g, o, q, L, 30.0, f"scale 30 W={window} bits={bits}")
     lens = np.full(B, L, np.int32)
     # 8 queries (32 rows: the short-chunk kernel on the full cache, the split read
-    # on the window) and 96 (384 rows: the band path).  At this scale the logits
-    # span about 200, so the band path's bf16 rounding of the dequantized keys
-    # (2^-9 relative) moves them by a few hundredths; it is held to the oracle
-    # over those bf16 values, the other paths to the exact oracle.
-    for C, ref_cache in ((8, o), (96, bf16_tile_oracle(o))):
+    # on the window) and 96 (384 rows: the prefill kernel), all against the exact
+    # oracle.
+    for C in (8, 96):
         qc = small_q_bits(913 + C, (B, Hq, C, D), 0.25)
         out = kvq.kvq_attn_prefill_chunk(g, q_dev(qc), torch.from_numpy(lens).cuda(), L, scale=30.0)
         torch.cuda.synchronize()
-        got = torch_bf16_to_f64(out)
-        assert_close(got, ref_cache.attend(qc, lens, scale=30.0), f"scale 30 chunk C={C} W={window} bits={bits}")
-        if ref_cache is not o:
-            band_within_rounding_bound(got, o, qc, lens, 30.0, f"scale 30 band C={C} W={window} bits={bits}")
+        assert_close(torch_bf16_to_f64(out), o.attend(qc, lens, scale=30.0), f"scale 30 chunk C={C} W={window} bits={bits}")
 
-
-def band_within_rounding_bound(got, o, q_bits, lens, scale, what):
-    """The band path against the EXACT oracle, at a tolerance derived from the bf16
-    rounding of the dequantized keys and values (each within 2^-9 relative of its
-    exact value): a key's logit moves by at most
-      eps_j = scale * 2^-9 * sum_d |q_d k_jd|,
-    so every ratio of softmax weights moves by at most a factor e^(2 max eps), and
-      |o' - o| <= (e^(2 max_j eps_j) - 1) max_j |v_j - o| + max_j |v'_j - v_j|,
-    plus the output's own bf16 rounding (2^-9 |o|) and fp32 accumulation (1e-4)."""
-    ref = o.attend(q_bits, lens, scale=scale)
-    kd, vd = o.dequant_k(), o.dequant_v()                  # [B][H][R][D], exact
-    qf = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    B, Hq, C, D = q_bits.shape
-    hpk = Hq // o.H
-    worst = 0.0
-    for b in range(B):
-        for hq in range(Hq):
-            for i in range(C):
-                p = int(lens[b]) - C + i
-                lo = max(0, p - o.window + 1) if o.window else 0
-                slots = np.arange(lo, p + 1) % o.R
-                k = kd[b, hq // hpk, slots]
-                v = vd[b, hq // hpk, slots]
-                eps = scale * 2.0 ** -9 * (np.abs(k) * np.abs(qf[b, hq, i])).sum(axis=1)
-                tol = (np.expm1(2 * eps.max()) * np.abs(v - ref[b, hq, i]).max() + 2.0 ** -9 * np.abs(v).max()
-                       + 2.0 ** -9 * np.abs(ref[b, hq, i]).max() + 1e-4)
-                err = np.abs(got[b, hq, i] - ref[b, hq, i]).max()
-                assert err <= tol, f"{what}: row ({b},{hq},{i}) error {err:.3e} above the bound {tol:.3e}"
-                worst = max(worst, err / tol)
-    print(f"{what}: largest error / bound {worst:.3f}", flush=True)
 
 
 @pytest.mark.parametrize("bits", BITS)
