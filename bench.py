@@ -407,6 +407,14 @@ def probe_ceilings():
             read_sweep.append([blocks, nt, round(gbs, 1)])
             if gbs > best_read:
                 best_read, read_cfg = gbs, {"blocks": blocks, "nontemporal": nt}
+    # workgroups that each stream their own run (a split-KV read's shape): the rate
+    # such a read can reach with 16 KB in flight per 256-thread workgroup
+    seg_sweep = []
+    for blocks, seg in ((460, 310 << 10), (512, 1 << 20), (1024, 1 << 20), (2048, 512 << 10)):
+        for nt in (0, 1):
+            probes.segment_read(src, seg, blocks, bool(nt), sink)
+            ms = min(time_ms(lambda: probes.segment_read(src, seg, blocks, bool(nt), sink)) for _ in range(3))
+            seg_sweep.append([blocks, seg >> 10, nt, round(blocks * seg / (ms * 1e-3) / 1e9, 1)])
     del src
     fsink = torch.empty(4096 * 256, dtype=torch.float32, device="cuda")
     best_mfma, mfma_cfg, mfma_sweep = 0.0, None, []
@@ -428,6 +436,7 @@ def probe_ceilings():
     return {"hbm_read_gbs": round(best_read, 1), "hbm_read_probe": read_cfg,
             "mfma_bf16_tflops": round(best_mfma, 1), "mfma_probe": mfma_cfg,
             "hbm_read_sweep [blocks, nontemporal, GB/s]": read_sweep,
+            "hbm_segment_read_sweep [blocks, KiB per block, nontemporal, GB/s]": seg_sweep,
             "mfma_sweep [shape 0=16x16x32 1=32x32x16, blocks, TFLOP/s]": mfma_sweep}
 
 

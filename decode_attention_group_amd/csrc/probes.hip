@@ -46,6 +46,29 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if (r == kNever) sink[blockIdx.x * 256 + threadIdx.x] = r;
 }
 
+// Each workgroup reads its own contiguous segment (as a split of a KV read does),
+// four 16-byte loads in flight per thread per iteration.
+template <bool NT>
+__global__ __launch_bounds__(256) void segment_read_kernel(const u32x4* __restrict__ src, size_t seg_vec,
+                                                           uint32_t* __restrict__ sink)
+{
+    constexpr int kUnroll = 4;
+    const u32x4* base = src + (size_t)blockIdx.x * seg_vec;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    size_t i = threadIdx.x;
+    for (; i + (kUnroll - 1) * 256 < seg_vec; i += 256 * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = NT ? __builtin_nontemporal_load(base + i + u * 256) : base[i + u * 256];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+    for (; i < seg_vec; i += 256) acc ^= base[i];
+    const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (r == kNever) sink[blockIdx.x * 256 + threadIdx.x] = r;
+}
+
 // SHAPE 0: v_mfma_f32_16x16x32_bf16 (16384 FLOP each), 8 accumulators per wave;
 // SHAPE 1: v_mfma_f32_32x32x16_bf16 (32768 FLOP each), 4 accumulators per wave.
 template <int SHAPE>
@@ -98,6 +121,18 @@ KVQ_API int kvq_probe_stream_read(const void* src, size_t bytes, int32_t blocks,
         stream_read_kernel<true><<<blocks, 256, 0, stream>>>(static_cast<const u32x4*>(src), n_vec, sink);
     else
         stream_read_kernel<false><<<blocks, 256, 0, stream>>>(static_cast<const u32x4*>(src), n_vec, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+KVQ_API int kvq_probe_segment_read(const void* src, size_t segment_bytes, int32_t blocks, int32_t nontemporal,
+                                   uint32_t* sink, hipStream_t stream)
+{
+    if (!src || !sink || blocks < 1 || (reinterpret_cast<uintptr_t>(src) & 15) || segment_bytes % 16) return 1;
+    const size_t seg_vec = segment_bytes / 16;
+    if (nontemporal)
+        segment_read_kernel<true><<<blocks, 256, 0, stream>>>(static_cast<const u32x4*>(src), seg_vec, sink);
+    else
+        segment_read_kernel<false><<<blocks, 256, 0, stream>>>(static_cast<const u32x4*>(src), seg_vec, sink);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -10,7 +10,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq_probes.so")
-EXPORTS = ("kvq_probe_stream_read", "kvq_probe_mfma_bf16", "kvq_probe_mfma_flops_per_iter")
+EXPORTS = ("kvq_probe_stream_read", "kvq_probe_segment_read", "kvq_probe_mfma_bf16", "kvq_probe_mfma_flops_per_iter")
 _lib = None
 
 
@@ -23,6 +23,8 @@ def load_library(path: str = LIB_PATH):
         P, i32 = ctypes.c_void_p, ctypes.c_int32
         lib.kvq_probe_stream_read.argtypes = [P, ctypes.c_size_t, i32, i32, P, P]
         lib.kvq_probe_stream_read.restype = ctypes.c_int
+        lib.kvq_probe_segment_read.argtypes = [P, ctypes.c_size_t, i32, i32, P, P]
+        lib.kvq_probe_segment_read.restype = ctypes.c_int
         lib.kvq_probe_mfma_bf16.argtypes = [i32, i32, i32, P, P]
         lib.kvq_probe_mfma_bf16.restype = ctypes.c_int
         lib.kvq_probe_mfma_flops_per_iter.argtypes = [i32, i32]
@@ -41,6 +43,15 @@ def stream_read(src: torch.Tensor, blocks: int, nontemporal: bool, sink: torch.T
                                               sink.data_ptr(), _stream())
     if st:
         raise RuntimeError(f"kvq_probe_stream_read: status {st}")
+
+
+def segment_read(src: torch.Tensor, segment_bytes: int, blocks: int, nontemporal: bool, sink: torch.Tensor):
+    if blocks * segment_bytes > src.numel() * src.element_size():
+        raise ValueError("segments past the buffer")
+    st = load_library().kvq_probe_segment_read(src.data_ptr(), segment_bytes, blocks, int(nontemporal),
+                                               sink.data_ptr(), _stream())
+    if st:
+        raise RuntimeError(f"kvq_probe_segment_read: status {st}")
 
 
 def mfma_bf16(shape: int, iters: int, blocks: int, sink: torch.Tensor) -> float:

@@ -31,6 +31,18 @@ int kvq_probe_stream_read(const void *src, size_t bytes, int32_t blocks, int32_t
                           uint32_t *sink, hipStream_t stream);
 
 /*
+ * Workgroup b of `blocks` (256 threads) reads bytes [b * segment_bytes,
+ * (b + 1) * segment_bytes) of `src` once, front to back, with 128-bit loads
+ * (non-temporal when `nontemporal` is 1): the access shape of a split-KV read,
+ * where each workgroup streams its own run of the cache.
+ *   src   16-byte aligned, at least blocks * segment_bytes bytes; segment_bytes a
+ *         multiple of 16
+ *   sink  uint32 [blocks * 256], written only under a condition the data never meets
+ */
+int kvq_probe_segment_read(const void *src, size_t segment_bytes, int32_t blocks, int32_t nontemporal,
+                           uint32_t *sink, hipStream_t stream);
+
+/*
  * Dense bf16 matrix-core loop: `blocks` workgroups of 4 waves, each wave
  * issuing `iters` rounds of independent MFMAs with fp32 accumulation:
  *   shape 0: 8 x v_mfma_f32_16x16x32_bf16 per round,
