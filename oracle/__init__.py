@@ -89,6 +89,10 @@ def _load():
         lib.kvqo_append_bf16.restype = i32
         lib.kvqo_bf16.argtypes = [ctypes.c_float]
         lib.kvqo_bf16.restype = ctypes.c_uint16
+        lib.kvqo_rms_factor.argtypes = [P, i32, ctypes.c_float]
+        lib.kvqo_rms_factor.restype = ctypes.c_float
+        lib.kvqo_norm_rows.argtypes = [P, ctypes.c_int64, i32, P, ctypes.c_float, P, P, i32, i32, P, P]
+        lib.kvqo_norm_rows.restype = i32
         lib.kvqo_max_threads.argtypes = []
         lib.kvqo_max_threads.restype = i32
         _lib = lib
@@ -217,6 +221,50 @@ def bf16_values(vals):
     """bf16 bit patterns -> fp64 values (exact)."""
     vals = np.ascontiguousarray(vals, dtype=np.uint16)
     return (vals.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rms_factor(x, eps: float) -> float:
+    """The RMS factor of one row: fp32(1 / sqrt(tree sum of squares / D + eps)) (kvq_oracle.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return float(_load().kvqo_rms_factor(_ptr(x), x.size, np.float32(eps)))
+
+
+def norm_rows(x, w=None, eps: float = 1e-6, rope=None, pos=None):
+    """Normalize rows of x (fp32 [..., D]) with the RMS norm (weight w [D] or none),
+    then, with rope = (cos [P][n/2], sin [P][n/2]), rotate the first n columns of
+    each row at its absolute position pos [...] (kvq_oracle.c kvqo_norm_rows)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    rows = x.size // D
+    y = np.zeros_like(x)
+    wp = None if w is None else np.ascontiguousarray(w, dtype=np.float32)
+    if rope is not None:
+        cos_t = np.ascontiguousarray(rope[0], dtype=np.float32)
+        sin_t = np.ascontiguousarray(rope[1], dtype=np.float32)
+        n_rot, n_pos = 2 * cos_t.shape[1], cos_t.shape[0]
+        pos = np.ascontiguousarray(np.broadcast_to(pos, x.shape[:-1]), dtype=np.int32)
+    else:
+        cos_t = sin_t = None
+        n_rot, n_pos = 0, 0
+    st = _load().kvqo_norm_rows(_ptr(x), rows, D, None if wp is None else _ptr(wp), np.float32(eps),
+                                None if cos_t is None else _ptr(cos_t), None if sin_t is None else _ptr(sin_t),
+                                n_rot, n_pos, None if pos is None else _ptr(pos), _ptr(y))
+    if st:
+        raise OracleError(st, "norm_rows")
+    return y
+
+
+def append_normed(cache: "Cache", k, v, pos0, k_weight, eps: float, rope=None):
+    """The fused step the library offers as kvq_append_norm_quantize: keys through
+    the weighted RMS norm and the rotation, values through the un-scaled norm,
+    then the append [p80 model.ts attentionTraining: kNorm, RoPE, vNorm, appendWindow]."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    B, H, T, D = k.shape
+    pos = (np.asarray(pos0, np.int64)[:, None, None] + np.arange(T)[None, None, :]) * np.ones((1, H, 1), np.int64)
+    kn = norm_rows(k, k_weight, eps, rope, pos.astype(np.int32))
+    vn = norm_rows(v, None, eps)
+    cache.append(kn, vn, pos0)
+    return kn, vn
 
 
 def attend_shared(cache: Cache, q_layers, len_, scale: float = 1.0, nthreads: int = 0):

@@ -357,6 +357,84 @@ int kvqo_attend_any(const uint8_t *k_codes, const uint16_t *k_scales, const uint
     return attend(&ks, &vs, B, Hkv, D, R, W, q, Hq, C, len, scale, out, nthreads);
 }
 
+/* ---------------------------------------------------------------------------
+ * Norm and rotation before the append [p80 model.ts attentionTraining: keys go
+ * through kNorm, then the cache's position rotation (RoPE), then appendWindow;
+ * values go through vNorm; p80 model.ts header: the value norm is an RMS norm
+ * without a learned scale].  The pages give neither the reduction order of the
+ * norm nor the rotation's frequencies (ProportionalRoPE is not on them), so
+ * this library fixes, for one row x[0..D) of one (token, head):
+ *   ss = sum of x_d^2 in fp64 over a complete binary tree: leaves in index
+ *        order, zero-padded to the next power of 2, each level adding pairs
+ *        (2i, 2i+1)
+ *   r  = fp32(1 / sqrt(ss / D + eps)), computed in fp64 and rounded once
+ *   y_d = fp32(x_d * r), then for keys fp32(y_d * w_d) with the norm's weight w
+ *   rotation (keys, when rope_dims > 0): with h = rope_dims / 2 and the caller's
+ *        table c = cos[pos][j], s = sin[pos][j] at the token's absolute position,
+ *        for j < h:  y_j' = fp32(fp32(y_j c) - fp32(y_{j+h} s)),
+ *                    y_{j+h}' = fp32(fp32(y_{j+h} c) + fp32(y_j s));
+ *        columns at and past rope_dims pass unchanged.
+ * Every fp32 step is one IEEE operation rounded to nearest even (no FMA). */
+static double tree_sumsq(const float *x, int n)
+{
+    double buf[512];
+    int P = 1;
+    while (P < n) P <<= 1;
+    for (int i = 0; i < P; ++i) buf[i] = i < n ? (double)x[i] * (double)x[i] : 0.0;
+    for (int w = P; w > 1; w >>= 1)
+        for (int i = 0; i < w / 2; ++i) buf[i] = buf[2 * i] + buf[2 * i + 1];
+    return buf[0];
+}
+
+/* The RMS factor r of one row (see above). */
+float kvqo_rms_factor(const float *x, int n, float eps)
+{
+    return (float)(1.0 / sqrt(tree_sumsq(x, n) / (double)n + (double)eps));
+}
+
+/* Normalize (and, with rope_dims > 0, rotate) `rows` rows of D values:
+ *   x, y   fp32 [rows][D] (may not alias)
+ *   w      fp32 [D] norm weight, or NULL for the un-scaled norm
+ *   pos    int32 [rows] absolute position of each row's token (used only by the
+ *          rotation); cos_tab, sin_tab fp32 [rope_positions][rope_dims / 2]
+ * Returns 1 for invalid arguments (D not in 1..512, rope_dims odd or > D, eps
+ * negative or not finite, a position outside the table, a non-finite input or
+ * a result above 1e38 in magnitude), else 0. */
+int kvqo_norm_rows(const float *x, int64_t rows, int D, const float *w, float eps,
+                   const float *cos_tab, const float *sin_tab, int rope_dims, int rope_positions,
+                   const int32_t *pos, float *y)
+{
+    if (D < 1 || D > 512 || rope_dims < 0 || rope_dims % 2 || rope_dims > D) return 1;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return 1;
+    if (rope_dims > 0 && (!cos_tab || !sin_tab || !pos)) return 1;
+    const int h = rope_dims / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * D;
+        float *yr = y + r * D;
+        for (int d = 0; d < D; ++d)
+            if (!(fabsf(xr[d]) <= KVQO_MAX_ABS)) return 1;
+        const float f = kvqo_rms_factor(xr, D, eps);
+        for (int d = 0; d < D; ++d) {
+            const float t = xr[d] * f;
+            yr[d] = w ? t * w[d] : t;
+        }
+        if (h > 0) {
+            if (pos[r] < 0 || pos[r] >= rope_positions) return 1;
+            const float *c = cos_tab + (int64_t)pos[r] * h;
+            const float *s = sin_tab + (int64_t)pos[r] * h;
+            for (int j = 0; j < h; ++j) {
+                const float a = yr[j], b = yr[j + h];
+                const float ac = a * c[j], bs = b * s[j], bc = b * c[j], as = a * s[j];
+                yr[j] = ac - bs;
+                yr[j + h] = bc + as;
+            }
+        }
+        for (int d = 0; d < D; ++d)
+            if (!(fabsf(yr[d]) <= KVQO_MAX_ABS)) return 1;
+    }
+    return 0;
+}
+
 /* Threads an OpenMP region would use (1 without OpenMP). */
 int kvqo_max_threads(void)
 {
