@@ -7,6 +7,7 @@ and the current stream.  There is no CPU fallback -- calls fail with
 
 Functions (same names as the C entry points):
   kvq_append_quantize(cache, k, v, pos0)
+  kvq_append_norm_quantize(cache, k, v, pos0, k_weight, eps, rope=None, k_out=None, v_out=None)
   kvq_attn_decode(cache, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_attn_prefill_chunk(cache, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_decode_step(cache, k, v, q, len, max_len, scale=1.0, out=None, workspace=None)
@@ -37,7 +38,7 @@ MAX_SHARED_GROUPS = 4
 SIZE_MAX = (1 << 64) - 1
 
 # Symbols include/kvq.h declares.
-EXPORTS = ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+EXPORTS = ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
            "kvq_attn_decode_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
            "kvq_decode_step_workspace_bytes", "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
            "kvq_last_error", "kvq_mark_next_read", "kvq_attn_decode_static")
@@ -93,6 +94,7 @@ def load_library(path: str = LIB_PATH):
     CP = ctypes.POINTER(CacheStruct)
     GP = ctypes.POINTER(SharedGroupStruct)
     lib.kvq_append_quantize.argtypes = [CP, P, P, i32, P, P]
+    lib.kvq_append_norm_quantize.argtypes = [CP, P, P, i32, P, P, ctypes.c_float, P, P, i32, i32, P, P, P]
     lib.kvq_attn_decode.argtypes = [CP, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_decode_step.argtypes = [CP, P, P, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_decode_step_workspace_bytes.argtypes = [CP, i32, i32]
@@ -113,7 +115,7 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_mark_next_read.restype = ctypes.c_int
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
-    for name in ("kvq_append_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+    for name in ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
                  "kvq_attn_decode_shared", "kvq_attn_mixed"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -204,6 +206,42 @@ def kvq_append_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: 
     if tuple(v.shape) != tuple(k.shape) or (B, H, D) != (cache.batch, cache.n_kv_heads, cache.head_dim):
         raise ValueError("k/v shape does not match the cache")
     _check(lib.kvq_append_quantize(ctypes.byref(cache.struct), _ptr(k), _ptr(v), T, _ptr(pos0), _stream()))
+
+
+def kvq_append_norm_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: torch.Tensor,
+                             k_weight: Optional[torch.Tensor], eps: float, rope=None,
+                             k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None):
+    """Norm (keys weighted by k_weight [D], values un-scaled), rotate the keys with
+    rope = (cos, sin) fp32 [positions][rope_dims/2] at absolute positions, then
+    quantize and append as kvq_append_quantize; k_out / v_out receive the normed rows."""
+    lib = load_library()
+    _gpu(k, "k", torch.float32)
+    _gpu(v, "v", torch.float32)
+    _gpu(pos0, "pos0", torch.int32)
+    B, H, T, D = k.shape
+    if tuple(v.shape) != tuple(k.shape) or (B, H, D) != (cache.batch, cache.n_kv_heads, cache.head_dim):
+        raise ValueError("k/v shape does not match the cache")
+    if k_weight is not None:
+        _gpu(k_weight, "k_weight", torch.float32)
+        if k_weight.numel() != D:
+            raise ValueError("k_weight must hold head_dim values")
+    cos_t = sin_t = None
+    rope_dims = rope_positions = 0
+    if rope is not None:
+        cos_t, sin_t = rope
+        _gpu(cos_t, "rope cos", torch.float32)
+        _gpu(sin_t, "rope sin", torch.float32)
+        if cos_t.dim() != 2 or tuple(sin_t.shape) != tuple(cos_t.shape):
+            raise ValueError("rope tables must both be [positions][rope_dims/2]")
+        rope_positions, rope_dims = cos_t.shape[0], 2 * cos_t.shape[1]
+    for name, o in (("k_out", k_out), ("v_out", v_out)):
+        if o is not None:
+            _gpu(o, name, torch.float32)
+            if tuple(o.shape) != tuple(k.shape):
+                raise ValueError(f"{name} must have k's shape")
+    _check(lib.kvq_append_norm_quantize(ctypes.byref(cache.struct), _ptr(k), _ptr(v), T, _ptr(pos0),
+                                        _ptr(k_weight), float(eps), _ptr(cos_t), _ptr(sin_t), rope_dims,
+                                        rope_positions, _ptr(k_out), _ptr(v_out), _stream()))
 
 
 def _group_struct(cache: KVCache, qs: Sequence[torch.Tensor], outs: Sequence[torch.Tensor],

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["append.hip", "attn.hip", "prefill.hip", "prefill_q.hip", "prefill_codes.hip", "bf16_cache.hip",
+SOURCES = ["append.hip", "append_norm.hip", "attn.hip", "prefill.hip", "prefill_q.hip", "prefill_codes.hip", "bf16_cache.hip",
            "kvq_api.hip"]
 # measurement probes (include/kvq_probes.h), a library of their own
 PROBE_LIB = os.path.join(HERE, "libkvq_probes.so")
@@ -17,7 +17,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-    "-fvisibility=hidden", "-ffp-contract=fast",
+    "-fvisibility=hidden",
+    # fused multiply-add wherever the source allows it, except where a pragma
+    # asks for one IEEE rounding per operation (the quantizer, the norms)
+    "-ffp-contract=fast-honor-pragmas",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in ordinary VGPRs: the softmax and the scale folds read

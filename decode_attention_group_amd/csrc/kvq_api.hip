@@ -365,18 +365,14 @@ KVQ_API kvq_status kvq_mark_next_read(hipEvent_t before, hipEvent_t after)
     return ok();
 }
 
-KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, const float* v,
-                                       int32_t T, const int32_t* pos0, hipStream_t stream)
+// The launch parameters of an append of T tokens (T > 0); a non-OK status (with
+// a message) when an argument is invalid.
+static kvq_status append_params(const kvq_cache* cache, const float* k, const float* v, int32_t T,
+                                const int32_t* pos0, const char* what, kvq::AppendParams& p, int& n_cand)
 {
-    const char* what = "kvq_append_quantize";
-    kvq_status st = check_cache(cache, what);
-    if (st != KVQ_OK) return st;
-    if (T < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: T %d < 0", what, T);
-    if (T == 0) return ok();
     if (!k || !v || !pos0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k, v or pos0 is NULL", what);
     if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k and v must be 16-byte aligned", what);
-    kvq::AppendParams p;
     p.k = k;
     p.v = v;
     p.k_codes = cache->k_codes;
@@ -393,8 +389,23 @@ KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, c
     p.v_bits = cache->v_bits;
     p.t_first = T > p.R ? T - p.R : 0;
     p.n_written = T - p.t_first;
-    const int n_cand = std::min(p.R / 8, (p.n_written + 7) / 8 + 1);
+    n_cand = std::min(p.R / 8, (p.n_written + 7) / 8 + 1);
     if (2 * (int64_t)p.B > 65535) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch %d too large", what, p.B);
+    return KVQ_OK;
+}
+
+KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, const float* v,
+                                       int32_t T, const int32_t* pos0, hipStream_t stream)
+{
+    const char* what = "kvq_append_quantize";
+    kvq_status st = check_cache(cache, what);
+    if (st != KVQ_OK) return st;
+    if (T < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: T %d < 0", what, T);
+    if (T == 0) return ok();
+    kvq::AppendParams p;
+    int n_cand = 0;
+    st = append_params(cache, k, v, T, pos0, what, p, n_cand);
+    if (st != KVQ_OK) return st;
     if (cache->k_bits == 16) {                    // bf16 cache: round and store, no quantizer
         if (trace_on())
             fprintf(stderr, "[kvq] %s (bf16): B=%d H=%d T=%d D=%d R=%d\n", what, p.B, p.H, T, p.D, p.R);
@@ -406,6 +417,46 @@ KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, c
         fprintf(stderr, "[kvq] %s: B=%d H=%d T=%d D=%d R=%d bits=%d/%d blocks=%d\n", what, p.B, p.H, T, p.D, p.R,
                 p.k_bits, p.v_bits, n_cand);
     const hipError_t e = kvq::launch_append(p, n_cand, stream);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+KVQ_API kvq_status kvq_append_norm_quantize(const kvq_cache* cache, const float* k, const float* v,
+                                            int32_t T, const int32_t* pos0, const float* k_weight, float eps,
+                                            const float* rope_cos, const float* rope_sin, int32_t rope_dims,
+                                            int32_t rope_positions, float* k_out, float* v_out,
+                                            hipStream_t stream)
+{
+    const char* what = "kvq_append_norm_quantize";
+    kvq_status st = check_cache(cache, what);
+    if (st != KVQ_OK) return st;
+    if (T < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: T %d < 0", what, T);
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", what);
+    if (rope_dims < 0 || rope_dims % 2 != 0 || rope_dims > cache->head_dim)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: rope_dims %d must be even and in [0, head_dim %d]", what,
+                    rope_dims, cache->head_dim);
+    if (rope_dims > 0 && (!rope_cos || !rope_sin || rope_positions < 1))
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: a rotation needs both tables and rope_positions >= 1", what);
+    if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k_out and v_out must be 16-byte aligned", what);
+    if (T == 0) return ok();
+    kvq::NormAppendParams P;
+    int n_cand = 0;
+    st = append_params(cache, k, v, T, pos0, what, P.a, n_cand);
+    if (st != KVQ_OK) return st;
+    P.k_weight = k_weight;
+    P.eps = eps;
+    P.rope_cos = rope_dims > 0 ? rope_cos : nullptr;
+    P.rope_sin = rope_dims > 0 ? rope_sin : nullptr;
+    P.rope_half = rope_dims / 2;
+    P.rope_positions = rope_dims > 0 ? rope_positions : 0;
+    P.k_out = k_out;
+    P.v_out = v_out;
+    if (trace_on())
+        fprintf(stderr, "[kvq] %s: B=%d H=%d T=%d D=%d R=%d bits=%d/%d rope=%d blocks=%d\n", what, P.a.B, P.a.H, T,
+                P.a.D, P.a.R, P.a.k_bits, P.a.v_bits, rope_dims, n_cand);
+    const hipError_t e = kvq::launch_append_norm(P, n_cand, stream);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
     return ok();
 }

@@ -22,6 +22,19 @@ struct AppendParams {
     int32_t n_written;    // tokens written per sequence
 };
 
+// The append with the keys' and values' norms and the keys' rotation in front.
+struct NormAppendParams {
+    AppendParams a;
+    const float* k_weight;     // [D] or null (un-scaled)
+    float eps;
+    const float* rope_cos;     // [rope_positions][rope_half]
+    const float* rope_sin;
+    int32_t rope_half;         // rotated pairs per row (0: no rotation)
+    int32_t rope_positions;
+    float* k_out;              // [B][H][T][D] normed (rotated) rows, or null
+    float* v_out;
+};
+
 // Rows of one (sequence, KV head) pair are the query rows that read it:
 //   decode / shared: row = layer * hpk + h   (hpk = Hq / Hkv query heads per KV head)
 //   prefill:         row = i * hpk + h       (i = query index in the chunk)
@@ -87,6 +100,7 @@ inline size_t part_floats(const AttnDesc& d)
 
 hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_append_bf16(const AppendParams& p, hipStream_t stream);
+hipError_t launch_append_norm(const NormAppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);

@@ -164,6 +164,53 @@ kvq_status kvq_append_quantize(const kvq_cache *cache,
                                hipStream_t stream);
 
 /*
+ * kvq_append_quantize with the norms and the rotation in front, in one kernel
+ * (page 80, gemma4/model.ts attentionTraining: keys through kNorm and then the
+ * rotary embedding at their cache positions, values through vNorm, then
+ * appendWindow; header notes: the value norm has no learned scale, and the
+ * rotation may cover only part of head_dim).
+ *   k, v     fp32 [B][H][T][D], the projections before their norms (v may equal
+ *            k, as where keys and values share one projection)
+ *   T, pos0  as kvq_append_quantize: token t of sequence b sits at absolute
+ *            position pos0[b] + t and goes to slot (pos0[b] + t) mod R
+ *   k_weight fp32 [D], the key norm's weight, applied as given (a norm that
+ *            scales by 1 + w takes 1 + w here); NULL for no weight
+ *   eps      the norms' epsilon, finite and >= 0
+ *   rope_cos, rope_sin  fp32 [rope_positions][rope_dims / 2]: the rotation
+ *            table, indexed by absolute position (the pages do not give the
+ *            angles; the caller's table fixes them)
+ *   rope_dims  even, 0..D: the first rope_dims columns of each key rotate, column
+ *            j paired with column j + rope_dims/2; 0 skips the rotation (tables
+ *            may then be NULL)
+ *   k_out, v_out  fp32 [B][H][T][D] or NULL: the normed (keys: rotated) rows of
+ *            the tokens this call writes (the last min(T, R) of each sequence);
+ *            other rows are left as they are
+ * Per row of D values x (keys and values alike):
+ *   r = 1 / sqrt(ss / D + eps), ss the sum of the squares, computed in fp64 and
+ *       rounded once to fp32 (ss adds the squares pairwise over the row padded
+ *       with zeros to a power of two);
+ *   y_d = x_d * r (keys: then * k_weight[d]), each product rounded to fp32;
+ *   keys, j < rope_dims/2, with c, s the table's entries j at the token's
+ *   position: y_j' = y_j c - y_{j+n} s, y_{j+n}' = y_{j+n} c + y_j s
+ *   (n = rope_dims/2; each product and sum rounded to fp32, no fused multiply-add);
+ * then the rows are quantized (bf16 caches: rounded) and stored exactly as by
+ * kvq_append_quantize.  Inputs must be finite with |x| <= 1e38; a row whose
+ * ss / D + eps is 0 (all zeros with eps 0) has no norm and leaves unspecified
+ * codes.  A position outside [0, rope_positions) reads the table's nearest
+ * row (no memory outside the table is read); its rotated columns are then
+ * unspecified.  Returns KVQ_ERR_INVALID_ARGUMENT for eps, rope_dims or the
+ * tables out of range, or k_out / v_out not 16-byte aligned.
+ */
+kvq_status kvq_append_norm_quantize(const kvq_cache *cache,
+                                    const float *k, const float *v,
+                                    int32_t T, const int32_t *pos0,
+                                    const float *k_weight, float eps,
+                                    const float *rope_cos, const float *rope_sin,
+                                    int32_t rope_dims, int32_t rope_positions,
+                                    float *k_out, float *v_out,
+                                    hipStream_t stream);
+
+/*
  * One decode read: one query per sequence attends the cache
  * (page 80, model.ts decode declaration and attentionTraining read.attend(q, scale)).
  *   q      bf16 [B][Hq][D]; query head hq reads KV head hq / (Hq/Hkv)

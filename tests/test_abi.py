@@ -129,6 +129,32 @@ def test_append_validation(lib):
     assert f(ctypes.byref(cache(head_dim=96)), FAKE, FAKE, 4, FAKE, None) == 2
 
 
+def test_normed_append_validation(lib):
+    c = cache(head_dim=128)
+    f = lib.kvq_append_norm_quantize
+    ok = dict(w=FAKE, eps=1e-6, cos=FAKE, sin=FAKE, n=64, P=100, ko=None, vo=None)
+
+    def call(T=4, k=FAKE, **kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(c), k, FAKE, T, FAKE, a["w"], a["eps"], a["cos"], a["sin"], a["n"], a["P"],
+                 a["ko"], a["vo"], None)
+    assert call(T=-1) == 1
+    assert call(T=0) == 0                                            # a no-op once the arguments check out
+    assert call(k=0) == 1
+    assert call(eps=-1e-6) == 1
+    assert call(eps=float("nan")) == 1
+    assert call(eps=float("inf")) == 1
+    assert call(n=3) == 1                                            # odd rope_dims
+    assert call(n=130) == 1                                          # rope_dims > head_dim
+    assert call(n=-2) == 1
+    assert call(cos=None) == 1 and call(sin=None) == 1
+    assert call(P=0) == 1
+    assert call(ko=FAKE + 8) == 1                                    # outputs 16-byte aligned
+    assert call(T=0, n=0, cos=None, sin=None, P=0, w=None) == 0      # no rotation, no weight
+    assert f(ctypes.byref(cache(head_dim=96)), FAKE, FAKE, 4, FAKE, None, 1e-6, None, None, 0, 0, None, None,
+             None) == 2
+
+
 def _group(c, n_layers=1, Hq=8, max_len=4096):
     qa = (ctypes.c_void_p * max(n_layers, 1))(*([FAKE] * max(n_layers, 1)))
     oa = (ctypes.c_void_p * max(n_layers, 1))(*([FAKE] * max(n_layers, 1)))
