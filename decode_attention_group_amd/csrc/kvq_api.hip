@@ -219,13 +219,86 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     d.n_items = (int)(items * d.S);
 }
 
+// Kernel path of a chunk read:
+//   decode: head_dim 128, or a short chunk over a short key range: the decode
+//     kernel with per-row positions (each 16-row tile reads the keys; for a
+//     window of a few hundred keys the re-reads are cheaper than the
+//     alternatives: 15.6 us against 18.1 us for 5 queries x 8 heads of B8 over
+//     a 512-key window);
+//   codes:  head_dim 256/512, up to 64 rows per KV head over more than 2048
+//     keys (speculative-verify windows on full layers): each workgroup holds
+//     all the rows, so every key is read once, and dequantizes each step into
+//     LDS once (prefill_codes.hip; 63 us against 98 us on the decode path for
+//     5 queries x 8 heads of B4 over 32768 keys of head_dim 512).  Inside a
+//     mixed launch such a read runs in a launch of its own (74 us against 90
+//     us for the whole mixed read of three decoding layers plus a 5-query
+//     verify over 16384 keys, B8, with traffic 1.18x the algorithmic bytes
+//     against 3.07x);
+//   band:   longer chunks: the chunk's key band is dequantized once into the
+//     workspace as bf16, then 32 query rows per workgroup (prefill.hip).
+// A bf16 cache takes the band path for chunks of more than 64 rows per KV head
+// (its band is a copy), else its own split kernel (bf16_cache.hip).
+enum class ChunkPath { kDecode, kCodes, kBand };
+
+ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
+{
+    const bool big = chunk > 1 && kvq::chunk_kernels_for(c->head_dim);
+    if (c->k_bits == 16) {                 // bf16 caches: the bf16 split kernel, or the band (no short-chunk kernel)
+        const char* f = getenv("KVQ_PREFILL_PATH");
+        if (f && *f) return big && f[0] == 'b' ? ChunkPath::kBand : ChunkPath::kDecode;
+        return big && (int64_t)chunk * (n_q_heads / c->n_kv_heads) > kvq::kCodesPrefillRows ? ChunkPath::kBand
+                                                                                           : ChunkPath::kDecode;
+    }
+    const int64_t rows = (int64_t)chunk * (n_q_heads / c->n_kv_heads);
+    const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "codes" / "decode": force (measurement)
+    if (e && *e) return !big ? ChunkPath::kDecode : e[0] == 'b' ? ChunkPath::kBand
+                                                  : e[0] == 'c' ? ChunkPath::kCodes : ChunkPath::kDecode;
+    if (!big || rows <= kvq::kRowTile) return ChunkPath::kDecode;
+    if (rows > kvq::kCodesPrefillRows) return ChunkPath::kBand;
+    const int64_t keys = c->window > 0 ? std::min<int64_t>((int64_t)c->window + chunk - 1, max_len) : max_len;
+    return keys > 2048 ? ChunkPath::kCodes : ChunkPath::kDecode;
+}
+
+// Short-chunk (codes) kernel plan of one read: one workgroup per (b, kv head,
+// 64-row block, split), n_items of them, in a launch of its own.
+void plan_codes_desc(const ReadSpec& r, kvq::AttnDesc& d)
+{
+    plan_read(r, 1, d);                           // shape fields
+    const kvq_cache* c = r.cache;
+    const int n_rb = (d.n_rows + kvq::kCodesPrefillRows - 1) / kvq::kCodesPrefillRows;
+    int64_t vis = r.max_len;
+    if (c->window > 0)
+        vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kCodesPrefillRows + d.hpk - 1) / d.hpk);
+    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
+    const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
+    // resident workgroups: two per CU for head_dim 256, one for 512 (its LDS)
+    const int kTargetWg = d.D == 512 ? 256 : 512;
+    int64_t S = (kTargetWg + items - 1) / items;
+    const int forced = env_splits();
+    if (forced > 0) S = forced;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
+    const int64_t steps_per = (steps + S - 1) / S;
+    d.split_len = (int)(steps_per * kvq::kStep);
+    d.S = (int)((steps + steps_per - 1) / steps_per);
+    d.n_items = (int)(items * d.S);
+    d.own_launch = 1;
+}
+
 size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
 {
     std::memset(&P, 0, sizeof(P));
     P.n_desc = n;
     double bytes[KVQ_MAX_SHARED_GROUPS];
     double total = 0.0;
+    // A chunk read that the short-chunk kernel serves best (see chunk_path) runs
+    // in a launch of its own, where every key is read once for all its rows; the
+    // other reads share one launch and its workgroup budget.
+    bool own[KVQ_MAX_SHARED_GROUPS];
+    for (int i = 0; i < n; ++i)
+        own[i] = rs[i].C > 1 && chunk_path(rs[i].cache, rs[i].Hq, rs[i].C, rs[i].max_len) == ChunkPath::kCodes;
     for (int i = 0; i < n; ++i) {
+        bytes[i] = 0.0;
+        if (own[i]) continue;
         const kvq_cache* c = rs[i].cache;
         const double per_key = c->head_dim * (c->k_bits + c->v_bits) / 8.0 + 4.0 * 2 * c->head_dim / 64;
         const double vis = c->window > 0 ? std::min(c->window, rs[i].max_len) : rs[i].max_len;
@@ -242,6 +315,8 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
     double free_bytes = 0.0;
     bool fixed[KVQ_MAX_SHARED_GROUPS];
     for (int i = 0; i < n; ++i) {
+        fixed[i] = false;
+        if (own[i]) continue;
         const kvq_cache* c = rs[i].cache;
         const int rows = (rs[i].C == 1 ? rs[i].n_layers : rs[i].C) * (rs[i].Hq / c->n_kv_heads);
         const int64_t items = (int64_t)c->batch * c->n_kv_heads * ((rows + kvq::kRowTile - 1) / kvq::kRowTile);
@@ -254,12 +329,17 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
     int comb = 0;
     size_t ws = 0;
     for (int i = 0; i < n; ++i) {
-        const double share = fixed[i] ? 0.0 : (free_bytes > 0 ? bytes[i] / free_bytes : 1.0);
-        const int target = std::max(1, (int)std::lround(free_wg * share));
         kvq::AttnDesc& d = P.d[i];
-        plan_read(rs[i], target, d);
-        d.item_begin = total_items;
-        total_items += d.n_items;
+        if (own[i]) {
+            plan_codes_desc(rs[i], d);
+            d.item_begin = 0;
+        } else {
+            const double share = fixed[i] ? 0.0 : (free_bytes > 0 ? bytes[i] / free_bytes : 1.0);
+            const int target = std::max(1, (int)std::lround(free_wg * share));
+            plan_read(rs[i], target, d);
+            d.item_begin = total_items;
+            total_items += d.n_items;
+        }
         d.comb_begin = comb;
         if (d.S > 1) comb += d.B * d.Hkv * d.n_rows * (d.D / 64);
         const size_t f = kvq::part_floats(d);
@@ -291,10 +371,15 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     if (reinterpret_cast<uintptr_t>(workspace) & 15)
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
     bind_workspace(P, workspace);
+    // the reads that share one launch, renumbered; the others launch alone
+    kvq::AttnParams Ps;
+    std::memset(&Ps, 0, sizeof(Ps));
+    for (int i = 0; i < n; ++i)
+        if (!P.d[i].own_launch) Ps.d[Ps.n_desc++] = P.d[i];
     bool same = true, big = true;
-    for (int i = 0; i < n; ++i) {
-        same &= P.d[i].cfg == P.d[0].cfg;
-        big &= kvq::chunk_kernels_for(P.d[i].D) && !kvq::cfg_is_bf16(P.d[i].cfg);
+    for (int i = 0; i < Ps.n_desc; ++i) {
+        same &= Ps.d[i].cfg == Ps.d[0].cfg;
+        big &= kvq::chunk_kernels_for(Ps.d[i].D) && !kvq::cfg_is_bf16(Ps.d[i].cfg);
     }
     auto launch_one = [&](const kvq::AttnParams& p, int items) {
         return kvq::cfg_is_bf16(p.d[0].cfg) ? kvq::launch_attn_bf16(p, items, stream)
@@ -302,25 +387,36 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     };
     if (trace_on())
         for (int i = 0; i < n; ++i)
-            fprintf(stderr, "[kvq] %s desc %d: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d tiles=%d S=%d split=%d wg=%d\n",
-                    what, i, P.d[i].B, P.d[i].Hkv, P.d[i].Hq, P.d[i].D, P.d[i].R, P.d[i].W, P.d[i].C,
-                    P.d[i].n_rows, P.d[i].n_rt, P.d[i].S, P.d[i].split_len, P.d[i].n_items);
+            fprintf(stderr, "[kvq] %s desc %d%s: B=%d Hkv=%d Hq=%d D=%d R=%d W=%d C=%d rows=%d tiles=%d S=%d split=%d wg=%d\n",
+                    what, i, P.d[i].own_launch ? " (short-chunk kernel)" : "", P.d[i].B, P.d[i].Hkv, P.d[i].Hq,
+                    P.d[i].D, P.d[i].R, P.d[i].W, P.d[i].C, P.d[i].n_rows, P.d[i].n_rt, P.d[i].S,
+                    P.d[i].split_len, P.d[i].n_items);
     hipError_t e = hipSuccess;
     mark_before(stream);
-    if (same) {
-        e = launch_one(P, total_items);
+    if (Ps.n_desc == 0) {
+        // every read runs in a launch of its own
+    } else if (same) {
+        e = launch_one(Ps, total_items);
     } else if (big) {
-        e = kvq::launch_attn(P, total_items, true, stream);
+        e = kvq::launch_attn(Ps, total_items, true, stream);
     } else {
         // Mixed configurations outside the fused set: one launch per descriptor.
-        for (int i = 0; i < n && e == hipSuccess; ++i) {
+        for (int i = 0; i < Ps.n_desc && e == hipSuccess; ++i) {
             kvq::AttnParams one;
             std::memset(&one, 0, sizeof(one));
             one.n_desc = 1;
-            one.d[0] = P.d[i];
+            one.d[0] = Ps.d[i];
             one.d[0].item_begin = 0;
-            e = launch_one(one, P.d[i].n_items);
+            e = launch_one(one, Ps.d[i].n_items);
         }
+    }
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+        if (!P.d[i].own_launch) continue;
+        kvq::AttnParams one;
+        std::memset(&one, 0, sizeof(one));
+        one.n_desc = 1;
+        one.d[0] = P.d[i];
+        e = kvq::launch_prefill_codes(one, P.d[i].n_items, stream);
     }
     mark_after(stream);
     if (e == hipSuccess) e = kvq::launch_combine(P, stream);
@@ -507,42 +603,6 @@ KVQ_API size_t kvq_decode_workspace_bytes(const kvq_shared_group* groups, int32_
     return plan_all(rs, n_groups, P, total);
 }
 
-// Kernel path of a chunk read:
-//   decode: head_dim 128, or a short chunk over a short key range: the decode
-//     kernel with per-row positions (each 16-row tile reads the keys; for a
-//     window of a few hundred keys the re-reads are cheaper than the
-//     alternatives: 15.6 us against 18.1 us for 5 queries x 8 heads of B8 over
-//     a 512-key window);
-//   codes:  head_dim 256/512, up to 64 rows per KV head over more than 2048
-//     keys (speculative-verify windows on full layers): each workgroup holds
-//     all the rows, so every key is read once, and dequantizes each step into
-//     LDS once (prefill_codes.hip; 88 us against 120 us on the decode path for
-//     5 queries x 8 heads of B4 over 32768 keys of head_dim 512);
-//   band:   longer chunks: the chunk's key band is dequantized once into the
-//     workspace as bf16, then 32 query rows per workgroup (prefill.hip).
-// A bf16 cache takes the band path for chunks of more than 64 rows per KV head
-// (its band is a copy), else its own split kernel (bf16_cache.hip).
-enum class ChunkPath { kDecode, kCodes, kBand };
-
-ChunkPath chunk_path(const kvq_cache* c, int n_q_heads, int chunk, int max_len)
-{
-    const bool big = chunk > 1 && kvq::chunk_kernels_for(c->head_dim);
-    if (c->k_bits == 16) {                 // bf16 caches: the bf16 split kernel, or the band (no short-chunk kernel)
-        const char* f = getenv("KVQ_PREFILL_PATH");
-        if (f && *f) return big && f[0] == 'b' ? ChunkPath::kBand : ChunkPath::kDecode;
-        return big && (int64_t)chunk * (n_q_heads / c->n_kv_heads) > kvq::kCodesPrefillRows ? ChunkPath::kBand
-                                                                                           : ChunkPath::kDecode;
-    }
-    const int64_t rows = (int64_t)chunk * (n_q_heads / c->n_kv_heads);
-    const char* e = getenv("KVQ_PREFILL_PATH");          // "band" / "codes" / "decode": force (measurement)
-    if (e && *e) return !big ? ChunkPath::kDecode : e[0] == 'b' ? ChunkPath::kBand
-                                                  : e[0] == 'c' ? ChunkPath::kCodes : ChunkPath::kDecode;
-    if (!big || rows <= kvq::kRowTile) return ChunkPath::kDecode;
-    if (rows > kvq::kCodesPrefillRows) return ChunkPath::kBand;
-    const int64_t keys = c->window > 0 ? std::min<int64_t>((int64_t)c->window + chunk - 1, max_len) : max_len;
-    return keys > 2048 ? ChunkPath::kCodes : ChunkPath::kDecode;
-}
-
 // Band positions per (b, kv head): every position a query of the chunk can see,
 // from a step-aligned start.
 int64_t band_positions(const kvq_cache* c, int chunk, int max_len)
@@ -632,25 +692,9 @@ size_t plan_codes(const ReadSpec& r, kvq::AttnParams& P, int& total_items)
 {
     std::memset(&P, 0, sizeof(P));
     P.n_desc = 1;
-    plan_read(r, 1, P.d[0]);                      // shape fields
     kvq::AttnDesc& d = P.d[0];
-    const kvq_cache* c = r.cache;
-    const int n_rb = (d.n_rows + kvq::kCodesPrefillRows - 1) / kvq::kCodesPrefillRows;
-    int64_t vis = r.max_len;
-    if (c->window > 0)
-        vis = std::min<int64_t>(vis, (int64_t)c->window + (kvq::kCodesPrefillRows + d.hpk - 1) / d.hpk);
-    const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
-    const int64_t items = (int64_t)d.B * d.Hkv * n_rb;
-    // resident workgroups: two per CU for head_dim 256, one for 512 (its LDS)
-    const int kTargetWg = d.D == 512 ? 256 : 512;
-    int64_t S = (kTargetWg + items - 1) / items;
-    const int forced = env_splits();
-    if (forced > 0) S = forced;
-    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, kvq::kMaxSplits)));
-    const int64_t steps_per = (steps + S - 1) / S;
-    d.split_len = (int)(steps_per * kvq::kStep);
-    d.S = (int)((steps + steps_per - 1) / steps_per);
-    d.n_items = (int)(items * d.S);
+    plan_codes_desc(r, d);
+    d.own_launch = 0;                             // the only descriptor of its launch
     total_items = d.n_items;
     return kvq::part_floats(d) * sizeof(float);
 }

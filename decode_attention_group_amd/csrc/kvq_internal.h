@@ -70,6 +70,8 @@ struct AttnDesc {
     int32_t comb_begin;     // first combine workgroup of this descriptor (S > 1)
     float scale_log2e;
     int32_t cfg;            // kernel configuration id (head_dim, k_bits, v_bits)
+    int32_t own_launch;     // host: a short chunk of a mixed launch, read by the codes
+                            // kernel in a launch of its own (items counted from 0)
 };
 
 struct AttnParams {

@@ -349,8 +349,12 @@ typedef struct {
  * Decode reads and short chunks of different caches in one attention launch
  * (plus one combine launch); each output equals that of the read alone
  * (kvq_attn_decode, or kvq_attn_prefill_chunk of the chunk) up to rounding.
- * 1 <= n_reads <= KVQ_MAX_SHARED_GROUPS; chunks run on the decode kernel, so a
- * chunk's rows (chunk x Hq/Hkv per KV head) are read in 16-row tiles.
+ * 1 <= n_reads <= KVQ_MAX_SHARED_GROUPS.  A chunk runs on the decode kernel
+ * (its rows, chunk x Hq/Hkv per KV head, read in 16-row tiles), except a
+ * chunk of 17 to 64 rows per KV head over more than 2048 keys at head_dim 256
+ * or 512 on a quantized cache: that one takes a launch of its own on the
+ * short-chunk kernel, which holds all its rows per workgroup and so reads
+ * each key once.
  */
 kvq_status kvq_attn_mixed(const kvq_read *reads, int32_t n_reads,
                           void *workspace, size_t workspace_bytes,
