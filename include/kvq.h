@@ -46,9 +46,10 @@
  *   - Alignment: cache arrays, k and v 16 bytes; q 16 bytes; out 8 bytes; a
  *     workspace 16 bytes (checked; INVALID_ARGUMENT otherwise).  batch <= 32767, n_kv_heads <= 65535.
  *   - Precision: products accumulate in fp32 and out is rounded once to bf16.
- *     On quantized caches, decode reads, the decode step, shared and mixed
- *     reads, and chunks of up to 16 query rows per KV head (rows = chunk *
- *     Hq/Hkv) multiply the codes exactly and take any finite q and any cache
+ *     On quantized caches, decode reads (alone, shared or mixed), the decode
+ *     step, and chunks of up to 16 query rows per KV head (rows = chunk *
+ *     Hq/Hkv; alone or in a mixed launch, as for every chunk rule below)
+ *     multiply the codes exactly and take any finite q and any cache
  *     the append wrote: q enters the fp16 MFMAs after a power of 2 per row and
  *     64-group (exact for every value within 2^-28 of the group's largest), and
  *     a step whose V scales reach 2^7 or V biases 2^15 runs its value product on
