@@ -176,6 +176,15 @@ class Runner:
                             for qs in wl.queries] for r in range(self.nrep)]
             nbytes = kvq.kvq_decode_workspace_bytes(
                 [(g.cache, g.q, g.out, g.len, g.max_len, g.scale) for g in self.groups[0]])
+            keep: list = []
+            arr = (kvq.SharedGroupStruct * len(self.groups[0]))(
+                *[kvq._group_struct(g.cache, g.q, g.out, g.len, g.max_len, g.scale, keep=keep)
+                  for g in self.groups[0]])
+            nbytes = max(nbytes, kvq.load_library().kvq_decode_step_shared_workspace_bytes(arr, len(self.groups[0])))
+            self.step_k = [self.step_kv[qs.cache][0].reshape(spec.B, spec.Hkv, spec.D)
+                           for qs in wl.queries for spec in [wl.cache(qs.cache)]]
+            self.step_v = [self.step_kv[qs.cache][1].reshape(spec.B, spec.Hkv, spec.D)
+                           for qs in wl.queries for spec in [wl.cache(qs.cache)]]
         elif wl.kind == "mixed":
             self.reads = [[kvq.Read(self.caches[qs.cache][r], self.q[qs.cache], self.len[qs.cache],
                                     wl.cache(qs.cache).length, 1.0, self.out[qs.cache])
@@ -192,7 +201,10 @@ class Runner:
             k, v = self.step_kv["kv"]
             self.step_k1 = k.reshape(spec.B, spec.Hkv, spec.D)
             self.step_v1 = v.reshape(spec.B, spec.Hkv, spec.D)
-        # decode steps run as one fused call (append + read); the others as two
+        # single-cache decode steps run as one fused call (append + read); the
+        # others as two (for the KV-shared groups, kvq_decode_step_shared measured
+        # 144 us against 130 us for the appends + kvq_attn_decode_shared: its new
+        # token's split makes the unsplit donor read go through the combine)
         self.fused = wl.kind == "decode"
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -216,7 +228,10 @@ class Runner:
                                 1.0, out=self.out["kv"][0], workspace=self.ws)
 
     def step(self, r):
-        """One decode step as the fused call: the token's append and the read."""
+        """One decode step as the fused call: the tokens' appends and the read."""
+        if self.wl.kind == "shared":
+            self.kvq.kvq_decode_step_shared(self.groups[r], self.step_k, self.step_v, workspace=self.ws)
+            return
         self.kvq.kvq_decode_step(self.caches["kv"][r], self.step_k1, self.step_v1, self.q["kv"][0],
                                  self.len["kv"], self.wl.caches[0].length, 1.0, out=self.out["kv"][0],
                                  workspace=self.ws)

@@ -12,6 +12,7 @@ Functions (same names as the C entry points):
   kvq_attn_prefill_chunk(cache, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_decode_step(cache, k, v, q, len, max_len, scale=1.0, out=None, workspace=None)
   kvq_attn_decode_shared(groups, workspace=None)
+  kvq_decode_step_shared(groups, k, v, workspace=None)
   kvq_attn_mixed(reads, workspace=None)
   kvq_decode_workspace_bytes(groups), kvq_decode_step_workspace_bytes(...),
   kvq_mixed_workspace_bytes(reads), kvq_prefill_workspace_bytes(...)
@@ -39,8 +40,9 @@ SIZE_MAX = (1 << 64) - 1
 
 # Symbols include/kvq.h declares.
 EXPORTS = ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
-           "kvq_attn_decode_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
-           "kvq_decode_step_workspace_bytes", "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
+           "kvq_attn_decode_shared", "kvq_decode_step_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
+           "kvq_decode_step_workspace_bytes", "kvq_decode_step_shared_workspace_bytes",
+           "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
            "kvq_last_error", "kvq_mark_next_read", "kvq_attn_decode_static")
 STATIC_SCRATCH_BYTES = 32 << 20
 
@@ -101,6 +103,9 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_decode_step_workspace_bytes.restype = sz
     lib.kvq_attn_prefill_chunk.argtypes = [CP, P, i32, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_attn_decode_shared.argtypes = [GP, i32, P, sz, P]
+    lib.kvq_decode_step_shared.argtypes = [GP, i32, P, P, P, sz, P]
+    lib.kvq_decode_step_shared_workspace_bytes.argtypes = [GP, i32]
+    lib.kvq_decode_step_shared_workspace_bytes.restype = sz
     RP = ctypes.POINTER(ReadStruct)
     lib.kvq_attn_mixed.argtypes = [RP, i32, P, sz, P]
     lib.kvq_mixed_workspace_bytes.argtypes = [RP, i32]
@@ -116,7 +121,7 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     for name in ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
-                 "kvq_attn_decode_shared", "kvq_attn_mixed"):
+                 "kvq_attn_decode_shared", "kvq_decode_step_shared", "kvq_attn_mixed"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -399,6 +404,43 @@ def kvq_attn_decode_shared(groups: Sequence[SharedGroup], workspace: Optional[to
     ws = _workspace(nbytes, workspace, device)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.kvq_attn_decode_shared(arr, len(specs), _ptr(ws), wsb, _stream()))
+    return [g.out for g in groups]
+
+
+def kvq_decode_step_shared(groups: Sequence[SharedGroup], k: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
+                           workspace: Optional[torch.Tensor] = None):
+    """Append k[i], v[i] fp32 [B][H][D] to group i's cache at position len-1 and run
+    the shared read of every group in one launch; returns the per-group output lists."""
+    lib = load_library()
+    if len(k) != len(groups) or len(v) != len(groups):
+        raise ValueError("one k and one v per group")
+    specs = []
+    for gi, g in enumerate(groups):
+        for i, q in enumerate(g.q):
+            _gpu(q, f"q[{i}]", torch.bfloat16)
+        _gpu(g.len, "len", torch.int32)
+        _gpu(k[gi], f"k[{gi}]", torch.float32)
+        _gpu(v[gi], f"v[{gi}]", torch.float32)
+        c = g.cache
+        if tuple(k[gi].shape) != (c.batch, c.n_kv_heads, c.head_dim) or tuple(v[gi].shape) != tuple(k[gi].shape):
+            raise ValueError(f"k[{gi}]/v[{gi}] shape does not match the cache")
+        if g.out is None:
+            g.out = [torch.empty_like(q) for q in g.q]
+        for i, o in enumerate(g.out):
+            _gpu(o, f"out[{i}]", torch.bfloat16)
+        specs.append((g.cache, g.q, g.out, g.len, g.max_len, g.scale))
+    keep: list = []
+    arr = (SharedGroupStruct * len(specs))(*[_group_struct(*s, keep=keep) for s in specs])
+    ka = (ctypes.c_void_p * len(k))(*[_ptr(t) for t in k])
+    va = (ctypes.c_void_p * len(v))(*[_ptr(t) for t in v])
+    nbytes = lib.kvq_decode_step_shared_workspace_bytes(arr, len(specs))
+    if nbytes == SIZE_MAX:
+        _check(lib.kvq_decode_step_shared(arr, len(specs), ka, va, None, 0, _stream()))
+        raise KvqError(1, "invalid arguments for kvq_decode_step_shared")
+    device = groups[0].q[0].device
+    ws = _workspace(nbytes, workspace, device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.kvq_decode_step_shared(arr, len(specs), ka, va, _ptr(ws), wsb, _stream()))
     return [g.out for g in groups]
 
 

@@ -117,8 +117,13 @@ constexpr float kRescaleSlack = 8.0f;
 // V words of the token's 8-slot block are read, merged and written while other
 // workgroups may be reading them: only the token's own bits change, so either
 // order gives them the other slots' codes.
+// (lds in the LDS address space: generic stores here could alias the kernel
+// arguments, which would then be copied to private memory)
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 template <int D, int KB, int VB>
-__device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float* lds)
+__device__ __forceinline__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, lds_f32* lds)
 {
     constexpr int NT = 64 * Shape<D>::NW;           // threads
     constexpr int G = D / 64, CH = D / 8, VW = VB / 4;
@@ -128,9 +133,9 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
     constexpr int EPP = D / PARTS;                  // elements per lane
     static_assert(2 * CH <= NT && EPP % 8 == 0 && EPP * PARTS == D, "one chunk per thread");
     static_assert((2 * D * 4 + D) <= (int)sizeof(AttnSmem<D>), "fits the attention LDS");
-    float* khat = lds;
-    float* vhat = lds + D;
-    uint8_t* vq = reinterpret_cast<uint8_t*>(lds + 2 * D);
+    lds_f32* khat = lds;
+    lds_f32* vhat = lds + D;
+    lds_u8* vq = reinterpret_cast<lds_u8*>(lds + 2 * D);
     const int tid = threadIdx.x;
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
     const int R = P.R;
@@ -152,7 +157,7 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
         uint32_t q[8];
         float scale, bias;
         quantize_group8(v, is_v ? (1 << VB) - 1 : (1 << KB) - 1, q, scale, bias);
-        float* xh = is_v ? vhat : khat;
+        lds_f32* xh = is_v ? vhat : khat;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xh[ch * 8 + e] = (float)q[e] * scale + bias;
         if (writer) {
@@ -182,8 +187,12 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
     const int grow = rt * kRowTile + r;
     const bool row_ok = r < kRowTile && grow < P.n_rows;
     const RowMap rm = map_row(P, hkv, row_ok ? grow : rt * kRowTile);
-    const uint16_t* qrow = as_global(P.q[0]) + ((((int64_t)b * P.Hq + rm.hq) * P.C + rm.qi) * D + part * EPP);
-    const float* kh = khat + part * EPP;
+    // the tile's rows may belong to several layers (a shared read): each row's own q
+    const int lay_lo = map_row(P, hkv, rt * kRowTile).layer;
+    const int lay_hi = map_row(P, hkv, min(rt * kRowTile + kRowTile, P.n_rows) - 1).layer;
+    const uint16_t* qrow = KVQ_LAYER_PTR(const uint16_t, P.q, lay_lo, lay_hi, rm.layer) +
+                           ((((int64_t)b * P.Hq + rm.hq) * P.C + rm.qi) * D + part * EPP);
+    const lds_f32* kh = khat + part * EPP;
     float acc = 0.0f;
 #pragma unroll
     for (int e0 = 0; e0 < EPP; e0 += 8) {
@@ -199,7 +208,8 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
     float* po = as_global(P.part) + prow * D + part * EPP;
 #pragma unroll
     for (int e0 = 0; e0 < EPP; e0 += 4)
-        *reinterpret_cast<f32x4*>(po + e0) = *reinterpret_cast<const f32x4*>(vhat + part * EPP + e0);
+        *reinterpret_cast<f32x4*>(po + e0) =
+            *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(vhat + part * EPP + e0);
     if (part == 0) {
         float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * P.S * kRowTile * D + prow * 2;
         pml[0] = acc * P.scale_log2e;
@@ -207,7 +217,8 @@ __device__ void new_token_split(const AttnDesc& P, int bh, int rt, int s, float*
     }
 }
 
-// STEP: the descriptor may be a fused decode step (single-descriptor launches only).
+// STEP: the descriptor may be a fused decode step (its k_new set); launches of
+// several descriptors route a step's new-token split before calling the body.
 template <int D, int KB, int VB, bool STEP = false>
 __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D>& sm)
 {
@@ -228,7 +239,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const int bh = idx / (S * P.n_rt);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
     if (STEP && P.k_new != nullptr && s == S - 1) {
-        new_token_split<D, KB, VB>(P, bh, rt, s, (float*)(__attribute__((address_space(3))) float*)(&sm));
+        new_token_split<D, KB, VB>(P, bh, rt, s, (lds_f32*)(&sm));
         return;
     }
     const int R = P.R, W = P.W, C = P.C;
@@ -721,8 +732,55 @@ __global__ __launch_bounds__(64 * Shape<D>::NW) void attn_kernel(AttnParams P)
         attn_body<D, KB, VB, true>(P.d[0], bid, sm);
     } else {
         const int di = find_desc(P, bid);
-        attn_body<D, KB, VB>(P.d[di], bid - P.d[di].item_begin, sm);
+        const AttnDesc& d = P.d[di];
+        const int idx = bid - d.item_begin;
+        if (d.k_new != nullptr && idx % d.S == d.S - 1) {     // a fused step's new-token split
+            new_token_split<D, KB, VB>(d, idx / (d.S * d.n_rt), (idx / d.S) % d.n_rt, d.S - 1,
+                                       (lds_f32*)(&sm));
+            return;
+        }
+        attn_body<D, KB, VB>(d, idx, sm);
     }
+}
+
+// The new-token splits of the fused-step descriptors of a launch that
+// attn_kernel_multi reads: one workgroup per (descriptor with k_new, sequence
+// and KV head, row tile), numbered over those descriptors in order.
+__global__ __launch_bounds__(256) void new_token_kernel(AttnParams P)
+{
+    __shared__ AttnSmem<512> sm;
+    int item = blockIdx.x, di = 0;
+    for (; di < P.n_desc; ++di) {
+        if (P.d[di].k_new == nullptr) continue;
+        const int n = P.d[di].B * P.d[di].Hkv * P.d[di].n_rt;
+        if (item < n) break;
+        item -= n;
+    }
+    if (di >= P.n_desc) return;
+    const AttnDesc& d = P.d[di];
+    const int bh = item / d.n_rt, rt = item % d.n_rt;
+    lds_f32* lds = (lds_f32*)(&sm);
+    switch (d.cfg) {
+    case cfg_of(256, 4, 4): new_token_split<256, 4, 4>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(256, 4, 8): new_token_split<256, 4, 8>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(256, 8, 4): new_token_split<256, 8, 4>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(256, 8, 8): new_token_split<256, 8, 8>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(512, 4, 4): new_token_split<512, 4, 4>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(512, 4, 8): new_token_split<512, 4, 8>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(512, 8, 4): new_token_split<512, 8, 4>(d, bh, rt, d.S - 1, lds); break;
+    case cfg_of(512, 8, 8): new_token_split<512, 8, 8>(d, bh, rt, d.S - 1, lds); break;
+    default: break;
+    }
+}
+
+hipError_t launch_new_tokens(const AttnParams& p, hipStream_t stream)
+{
+    int items = 0;
+    for (int i = 0; i < p.n_desc; ++i)
+        if (p.d[i].k_new != nullptr) items += p.d[i].B * p.d[i].Hkv * p.d[i].n_rt;
+    if (items == 0) return hipSuccess;
+    new_token_kernel<<<dim3(items), dim3(256), 0, stream>>>(p);
+    return hipGetLastError();
 }
 
 // One launch over descriptors of different configurations: the Gemma 4 decode
@@ -737,6 +795,9 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
     const int di = find_desc(P, bid);
     const AttnDesc& d = P.d[di];
     const int idx = bid - d.item_begin;
+    // a fused step's new-token splits run in a launch of their own (new_token_kernel):
+    // inlined here they would push this kernel past 256 registers
+    if (d.k_new != nullptr && idx % d.S == d.S - 1) return;
     switch (d.cfg) {
     case cfg_of(256, 4, 4): attn_body<256, 4, 4>(d, idx, sm256); break;
     case cfg_of(256, 4, 8): attn_body<256, 4, 8>(d, idx, sm256); break;

@@ -196,6 +196,7 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
     int64_t S = (target_wg + items - 1) / items;
+    if (r.k_new) S = std::max<int64_t>(1, S - 1);     // the new token's split counts against the target
     // two steps per split where that still leaves 128 workgroups: a workgroup's
     // first step costs a full memory round trip, its second overlaps it
     // (measured on 8 sequences x 2 KV heads over a 512-key window: 11.3 us at 9
@@ -319,7 +320,9 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         if (own[i]) continue;
         const kvq_cache* c = rs[i].cache;
         const int rows = (rs[i].C == 1 ? rs[i].n_layers : rs[i].C) * (rs[i].Hq / c->n_kv_heads);
-        const int64_t items = (int64_t)c->batch * c->n_kv_heads * ((rows + kvq::kRowTile - 1) / kvq::kRowTile);
+        // (a fused step's read takes one more workgroup per item, for the new token)
+        const int64_t items = (int64_t)c->batch * c->n_kv_heads * ((rows + kvq::kRowTile - 1) / kvq::kRowTile) *
+                              (rs[i].k_new ? 2 : 1);
         fixed[i] = total > 0 && items >= kTargetWg * (bytes[i] / total);
         if (fixed[i]) fixed_wg += (int)std::min<int64_t>(items, kTargetWg);
         else free_bytes += bytes[i];
@@ -398,7 +401,8 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     } else if (same) {
         e = launch_one(Ps, total_items);
     } else if (big) {
-        e = kvq::launch_attn(Ps, total_items, true, stream);
+        e = kvq::launch_new_tokens(Ps, stream);   // (fused steps only)
+        if (e == hipSuccess) e = kvq::launch_attn(Ps, total_items, true, stream);
     } else {
         // Mixed configurations outside the fused set: one launch per descriptor.
         for (int i = 0; i < Ps.n_desc && e == hipSuccess; ++i) {
@@ -892,5 +896,67 @@ KVQ_API kvq_status kvq_attn_decode_shared(const kvq_shared_group* groups, int32_
         kvq_status st = check_read(rs[i], what);
         if (st != KVQ_OK) return st;
     }
+    return run_reads(rs, n_groups, workspace, workspace_bytes, stream, what);
+}
+
+// ReadSpecs of a fused shared step; a non-OK status (with a message) when an
+// argument is invalid.  sizing: only what the workspace query can check.
+static kvq_status step_shared_specs(const kvq_shared_group* groups, int32_t n, const float* const* k,
+                                    const float* const* v, ReadSpec* rs, const char* what, bool sizing)
+{
+    static const float dummy = 0.0f;
+    if (!groups) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: groups is NULL", what);
+    if (n < 1 || n > KVQ_MAX_SHARED_GROUPS)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_groups %d outside [1, %d]", what, n, KVQ_MAX_SHARED_GROUPS);
+    if (!sizing && (!k || !v)) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: k or v is NULL", what);
+    for (int i = 0; i < n; ++i) {
+        const kvq_shared_group& g = groups[i];
+        const float* ki = sizing ? &dummy : k[i];
+        const float* vi = sizing ? &dummy : v[i];
+        rs[i] = ReadSpec{g.cache, g.n_layers, g.q, g.out, g.n_q_heads, g.scale, g.len, g.max_len, 1, ki, vi};
+        kvq_status st;
+        if (sizing) {
+            st = check_cache(g.cache, what);
+            if (st == KVQ_OK && (g.n_layers < 1 || g.n_layers > KVQ_MAX_SHARED_LAYERS || g.n_q_heads < 1 ||
+                                 g.n_q_heads % g.cache->n_kv_heads != 0 || g.max_len < 1))
+                st = fail(KVQ_ERR_INVALID_ARGUMENT, "%s: group %d: invalid read", what, i);
+        } else {
+            st = check_read(rs[i], what);
+        }
+        if (st != KVQ_OK) return st;
+        if (!sizing) {
+            if (!ki || !vi) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: group %d: k or v is NULL", what, i);
+            if ((reinterpret_cast<uintptr_t>(ki) | reinterpret_cast<uintptr_t>(vi)) & 15)
+                return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: group %d: k and v must be 16-byte aligned", what, i);
+        }
+        // each group appends to its own cache: two groups on one cache would write
+        // the same slot twice
+        for (int j = 0; j < i; ++j)
+            if (groups[j].cache->k_codes == g.cache->k_codes)
+                return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: groups %d and %d share a cache", what, j, i);
+    }
+    return KVQ_OK;
+}
+
+KVQ_API size_t kvq_decode_step_shared_workspace_bytes(const kvq_shared_group* groups, int32_t n_groups)
+{
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    if (step_shared_specs(groups, n_groups, nullptr, nullptr, rs, "kvq_decode_step_shared_workspace_bytes", true) !=
+        KVQ_OK)
+        return SIZE_MAX;
+    kvq::AttnParams P;
+    int total = 0;
+    return plan_all(rs, n_groups, P, total);
+}
+
+KVQ_API kvq_status kvq_decode_step_shared(const kvq_shared_group* groups, int32_t n_groups, const float* const* k,
+                                          const float* const* v, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream)
+{
+    MarkScope marks;
+    const char* what = "kvq_decode_step_shared";
+    ReadSpec rs[KVQ_MAX_SHARED_GROUPS];
+    const kvq_status st = step_shared_specs(groups, n_groups, k, v, rs, what, false);
+    if (st != KVQ_OK) return st;
     return run_reads(rs, n_groups, workspace, workspace_bytes, stream, what);
 }

@@ -106,6 +106,8 @@ hipError_t launch_append_norm(const NormAppendParams& p, int n_cand, hipStream_t
 hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
+// The new-token splits of fused-step descriptors read by launch_attn(..., multi=true).
+hipError_t launch_new_tokens(const AttnParams& p, hipStream_t stream);
 // The chunk's band tiles (dequantized, or a bf16 copy) when the prefill kernel
 // needs them; then the prefill kernel itself.
 hipError_t launch_band(const AttnParams& p, hipStream_t stream);

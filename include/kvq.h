@@ -325,6 +325,30 @@ kvq_status kvq_attn_decode_shared(const kvq_shared_group *groups, int32_t n_grou
                                   hipStream_t stream);
 
 /*
+ * One decode step of several donors and their sharers (page 80, model.ts
+ * header: KV-shared layers; attentionTraining: each donor appends its new keys
+ * and values, then every layer reading that cache attends it; decode
+ * declaration: one new token per sequence).  Equivalent to
+ *   kvq_append_quantize(groups[i].cache, k[i], v[i], 1, pos0 = len_i - 1) for
+ *   every group, followed by kvq_attn_decode_shared(groups, ...),
+ * with the same codes written bit for bit, in one attention launch (plus the
+ * combine): in each group the new token is quantized, written and attended
+ * from its dequantized values by one more split per KV head, as in
+ * kvq_decode_step.
+ *   groups  as for kvq_attn_decode_shared; each group's len counts the new token,
+ *           and no two groups may name the same cache (INVALID_ARGUMENT)
+ *   k, v    (host arrays of n_groups device pointers) fp32 [B][H][D] of group i's
+ *           cache, 16-byte aligned, finite with |x| <= 1e38: the keys (after
+ *           norm and RoPE) and values of the token at position len[b] - 1
+ *   workspace  at least kvq_decode_step_shared_workspace_bytes() bytes; needs no
+ *           clearing
+ */
+kvq_status kvq_decode_step_shared(const kvq_shared_group *groups, int32_t n_groups,
+                                  const float *const *k, const float *const *v,
+                                  void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
  * (host) One read of a mixed launch: like kvq_shared_group, plus the number of
  * queries per sequence.  chunk == 1 is a decode read by n_layers layers; chunk
  * > 1 is a short causal chunk (a speculative-verify window: query i of
@@ -372,6 +396,10 @@ size_t kvq_decode_workspace_bytes(const kvq_shared_group *groups, int32_t n_grou
 /* (host) Workspace bytes for kvq_decode_step with these arguments (SIZE_MAX when
  * they are invalid). */
 size_t kvq_decode_step_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads, int32_t max_len);
+
+/* (host) Workspace bytes for kvq_decode_step_shared with these groups (SIZE_MAX
+ * when they are invalid). */
+size_t kvq_decode_step_shared_workspace_bytes(const kvq_shared_group *groups, int32_t n_groups);
 
 /* (host) Workspace bytes for kvq_attn_prefill_chunk with these arguments. */
 size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads,

@@ -23,13 +23,16 @@ def q_dev(bits: np.ndarray) -> torch.Tensor:
 def clone_cache(g: kvq.KVCache) -> kvq.KVCache:
     c = kvq.KVCache(g.batch, g.n_kv_heads, g.head_dim, g.k_bits, g.v_bits, g.capacity, window=g.window)
     for src, dst in ((g.k_codes, c.k_codes), (g.v_codes, c.v_codes), (g.k_sb, c.k_sb), (g.v_sb, c.v_sb)):
-        dst.copy_(src)
+        if src is not None:                   # (a bf16 cache has no scale|bias arrays)
+            dst.copy_(src)
     return c
 
 
 def assert_same_cache(a: kvq.KVCache, b: kvq.KVCache, what: str):
     for name in ("k_codes", "v_codes", "k_sb", "v_sb"):
         x, y = getattr(a, name), getattr(b, name)
+        if x is None and y is None:
+            continue
         assert torch.equal(x, y), f"{what}: {name} differs in {(x != y).sum().item()} words"
 
 
@@ -141,3 +144,116 @@ def test_decode_step_rejects_bad_arguments():
         kvq.kvq_decode_step(g, k, k, q, lens, 65)               # full layer cannot hold 65
     with pytest.raises(kvq.KvqError):
         kvq.kvq_decode_step(g, k, k, torch.zeros(1, 3, 256, dtype=torch.bfloat16, device="cuda"), lens, 1)
+
+
+# ---- fused step of several shared groups (kvq_decode_step_shared)
+
+SHARED_STEP_GROUPS = [
+    # Hkv, D, kb, vb, R, W, layers, Hq
+    (2, 256, 4, 4, 512, 300, 3, 8),     # sliding donor with three sharing layers (ring)
+    (1, 512, 8, 8, 1024, 0, 1, 8),      # full donor, head_dim 512
+    (2, 128, 8, 4, 256, 200, 2, 4),     # a head_dim outside the two-configuration launch
+    (1, 256, 16, 16, 512, 512, 2, 4),   # a bf16 cache
+]
+
+
+@pytest.mark.parametrize("n_groups", [2, 4])
+def test_decode_step_shared_small(n_groups):
+    """Each group's cache equals kvq_append_quantize's for the same token; every
+    layer's output is within tolerance of the oracle after the oracle's append.
+    Ragged lengths: the second sequence is one position behind."""
+    B, L = 2, 600
+    lens_np = np.array([L + 1, L], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    groups, refs, caches, ks, vs = [], [], [], [], []
+    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(SHARED_STEP_GROUPS[:n_groups]):
+        g, o = history(B, Hkv, D, kb, vb, R, W, L, seed=500 + 10 * gi)
+        k = small_randn(600 + gi, (B, Hkv, D), D ** -0.25)
+        v = small_randn(700 + gi, (B, Hkv, D), D ** -0.25)
+        ref_cache = clone_cache(g)
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        kvq.kvq_append_quantize(ref_cache, kd[:, :, None].contiguous(), vd[:, :, None].contiguous(), lens - 1)
+        o.append(k[:, :, None], v[:, :, None], lens_np - 1)
+        qs = [small_q_bits(800 + 10 * gi + l, (B, Hq, 1, D), D ** -0.25) for l in range(layers)]
+        groups.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens, L + 1))
+        refs.append([o.attend(x, lens_np)[:, :, 0] for x in qs])
+        caches.append((g, ref_cache))
+        ks.append(kd)
+        vs.append(vd)
+    print(f"shared decode step, {n_groups} groups", flush=True)
+    outs = kvq.kvq_decode_step_shared(groups, ks, vs)
+    torch.cuda.synchronize()
+    for gi, (g, ref_cache) in enumerate(caches):
+        assert_same_cache(g, ref_cache, f"group {gi}")
+        for l, ref in enumerate(refs[gi]):
+            assert_close(torch_bf16_to_f64(outs[gi][l]), ref, f"group {gi} layer {l}")
+
+
+def test_decode_step_shared_matches_two_calls():
+    """Against appends followed by kvq_attn_decode_shared on copies of the caches:
+    the same caches word for word, outputs within the attention tolerance."""
+    B, L = 3, 900
+    lens = torch.full((B,), L + 1, dtype=torch.int32, device="cuda")
+    specs = SHARED_STEP_GROUPS[:2]
+    ga, gb, ks, vs, qss = [], [], [], [], []
+    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(specs):
+        g, _ = history(B, Hkv, D, kb, vb, R, W, L, seed=900 + gi)
+        ga.append(g)
+        gb.append(clone_cache(g))
+        ks.append(torch.from_numpy(small_randn(910 + gi, (B, Hkv, D), 0.25)).cuda())
+        vs.append(torch.from_numpy(small_randn(920 + gi, (B, Hkv, D), 0.25)).cuda())
+        qss.append([q_dev(small_q_bits(930 + 10 * gi + l, (B, Hq, D), 0.25)) for l in range(layers)])
+    print("shared decode step vs two calls", flush=True)
+    outs = kvq.kvq_decode_step_shared([kvq.SharedGroup(g, qs, lens, L + 1) for g, qs in zip(ga, qss)], ks, vs)
+    for g, k, v in zip(gb, ks, vs):
+        kvq.kvq_append_quantize(g, k[:, :, None].contiguous(), v[:, :, None].contiguous(), lens - 1)
+    outs2 = kvq.kvq_attn_decode_shared([kvq.SharedGroup(g, qs, lens, L + 1) for g, qs in zip(gb, qss)])
+    torch.cuda.synchronize()
+    for gi in range(len(specs)):
+        assert_same_cache(ga[gi], gb[gi], f"group {gi}")
+        for x, y in zip(outs[gi], outs2[gi]):
+            d = torch_bf16_to_f64(x) - torch_bf16_to_f64(y)
+            assert np.abs(d).max() <= 1e-2 and np.abs(d).mean() <= 1e-3
+
+
+def test_decode_step_shared_workload():
+    """The KV-shared decode workload as a fused step: its last position is the
+    step's token (appended by the step), every batch row checked."""
+    wl = WORKLOADS["shared_decode_b32"]
+    print("shared decode step workload shared_decode_b32", flush=True)
+    gpu, orc, qd, last = build_workload(wl, hold_last=True)
+    donor, full = wl.cache("donor"), wl.cache("full")
+    lens_np = np.full(donor.B, donor.length, np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    refs = {}
+    for name in ("donor", "full"):
+        ref_cache = clone_cache(gpu[name])
+        kvq.kvq_append_quantize(ref_cache, last[name][0], last[name][1], lens - 1)
+        refs[name] = ref_cache
+    qa = [q_dev(x[:, :, 0].copy()) for x in qd[0]]
+    qb = [q_dev(x[:, :, 0].copy()) for x in qd[1]]
+    outs = kvq.kvq_decode_step_shared(
+        [kvq.SharedGroup(gpu["donor"], qa, lens, donor.length), kvq.SharedGroup(gpu["full"], qb, lens, full.length)],
+        [last["donor"][0][:, :, 0].contiguous(), last["full"][0][:, :, 0].contiguous()],
+        [last["donor"][1][:, :, 0].contiguous(), last["full"][1][:, :, 0].contiguous()])
+    torch.cuda.synchronize()
+    for name in ("donor", "full"):
+        assert_same_cache(gpu[name], refs[name], name)
+    od, _ = orc["donor"]
+    for i, x in enumerate(qd[0]):
+        assert_close(torch_bf16_to_f64(outs[0][i]), od.attend(x, lens_np)[:, :, 0], f"donor layer {i}")
+    of, _ = orc["full"]
+    assert_close(torch_bf16_to_f64(outs[1][0]), of.attend(qd[1][0], lens_np)[:, :, 0], "full layer")
+
+
+def test_decode_step_shared_rejects_bad_arguments():
+    g = kvq.KVCache(1, 2, 256, 4, 4, 64)
+    k = torch.zeros(1, 2, 256, device="cuda")
+    q = torch.zeros(1, 8, 256, dtype=torch.bfloat16, device="cuda")
+    lens = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(kvq.KvqError):                     # two groups on one cache
+        kvq.kvq_decode_step_shared([kvq.SharedGroup(g, [q], lens, 1), kvq.SharedGroup(g, [q], lens, 1)],
+                                   [k, k], [k, k])
+    with pytest.raises(kvq.KvqError):                     # k not 16-byte aligned
+        kb = torch.zeros(1 * 2 * 256 + 1, device="cuda")[1:].view(1, 2, 256)
+        kvq.kvq_decode_step_shared([kvq.SharedGroup(g, [q], lens, 1)], [kb], [k])
