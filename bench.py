@@ -2,8 +2,9 @@
 """Benchmark of quantized-KV attention on one MI355X.
 
 A step is one pass of the hot path over one batch of the workload: the step's
-new token(s) are quantized and appended to the cache (kvq_append_quantize, or
-the fused kvq_decode_step on decode workloads), then the read runs
+new token(s) are quantized and appended to the cache (kvq_append_quantize, one
+kvq_append_quantize_multi launch for workloads with several caches, or the
+fused kvq_decode_step on decode workloads), then the read runs
 (kvq_attn_decode / kvq_attn_prefill_chunk / kvq_attn_decode_shared /
 kvq_attn_mixed).  Inputs are resident in HBM before timing starts.
 
@@ -210,9 +211,12 @@ class Runner:
         torch.cuda.synchronize()
 
     def append(self, r):
-        for spec in self.wl.caches:
-            k, v = self.step_kv[spec.name]
-            self.kvq.kvq_append_quantize(self.caches[spec.name][r], k, v, self.pos_new[spec.name])
+        """The step's tokens into every cache: one launch for several caches."""
+        items = [(self.caches[s.name][r], *self.step_kv[s.name], self.pos_new[s.name]) for s in self.wl.caches]
+        if len(items) > 1:
+            self.kvq.kvq_append_quantize_multi(items)
+        else:
+            self.kvq.kvq_append_quantize(*items[0])
 
     def attend(self, r):
         kvq, wl = self.kvq, self.wl

@@ -39,7 +39,7 @@ MAX_SHARED_GROUPS = 4
 SIZE_MAX = (1 << 64) - 1
 
 # Symbols include/kvq.h declares.
-EXPORTS = ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+EXPORTS = ("kvq_append_quantize", "kvq_append_quantize_multi", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
            "kvq_attn_decode_shared", "kvq_decode_step_shared", "kvq_attn_mixed", "kvq_decode_workspace_bytes",
            "kvq_decode_step_workspace_bytes", "kvq_decode_step_shared_workspace_bytes",
            "kvq_mixed_workspace_bytes", "kvq_prefill_workspace_bytes",
@@ -73,6 +73,11 @@ class SharedGroupStruct(ctypes.Structure):
                 ("len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
 
 
+class AppendItemStruct(ctypes.Structure):
+    _fields_ = [("cache", ctypes.POINTER(CacheStruct)), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("T", ctypes.c_int32), ("pos0", ctypes.c_void_p)]
+
+
 class ReadStruct(ctypes.Structure):
     _fields_ = [("cache", ctypes.POINTER(CacheStruct)), ("n_layers", ctypes.c_int32),
                 ("q", ctypes.POINTER(ctypes.c_void_p)), ("out", ctypes.POINTER(ctypes.c_void_p)),
@@ -96,6 +101,7 @@ def load_library(path: str = LIB_PATH):
     CP = ctypes.POINTER(CacheStruct)
     GP = ctypes.POINTER(SharedGroupStruct)
     lib.kvq_append_quantize.argtypes = [CP, P, P, i32, P, P]
+    lib.kvq_append_quantize_multi.argtypes = [ctypes.POINTER(AppendItemStruct), i32, P]
     lib.kvq_append_norm_quantize.argtypes = [CP, P, P, i32, P, P, ctypes.c_float, P, P, i32, i32, P, P, P]
     lib.kvq_attn_decode.argtypes = [CP, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
     lib.kvq_decode_step.argtypes = [CP, P, P, P, i32, P, i32, ctypes.c_float, P, P, sz, P]
@@ -120,7 +126,7 @@ def load_library(path: str = LIB_PATH):
     lib.kvq_mark_next_read.restype = ctypes.c_int
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
-    for name in ("kvq_append_quantize", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
+    for name in ("kvq_append_quantize", "kvq_append_quantize_multi", "kvq_append_norm_quantize", "kvq_attn_decode", "kvq_decode_step", "kvq_attn_prefill_chunk",
                  "kvq_attn_decode_shared", "kvq_decode_step_shared", "kvq_attn_mixed"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -211,6 +217,22 @@ def kvq_append_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: 
     if tuple(v.shape) != tuple(k.shape) or (B, H, D) != (cache.batch, cache.n_kv_heads, cache.head_dim):
         raise ValueError("k/v shape does not match the cache")
     _check(lib.kvq_append_quantize(ctypes.byref(cache.struct), _ptr(k), _ptr(v), T, _ptr(pos0), _stream()))
+
+
+def kvq_append_quantize_multi(items):
+    """Several appends in one launch: items = [(cache, k, v, pos0), ...], each as
+    kvq_append_quantize takes them; every item names its own cache."""
+    lib = load_library()
+    arr = (AppendItemStruct * max(1, len(items)))()
+    for i, (cache, k, v, pos0) in enumerate(items):
+        _gpu(k, "k", torch.float32)
+        _gpu(v, "v", torch.float32)
+        _gpu(pos0, "pos0", torch.int32)
+        B, H, T, D = k.shape
+        if tuple(v.shape) != tuple(k.shape) or (B, H, D) != (cache.batch, cache.n_kv_heads, cache.head_dim):
+            raise ValueError(f"item {i}: k/v shape does not match the cache")
+        arr[i] = AppendItemStruct(ctypes.pointer(cache.struct), _ptr(k), _ptr(v), T, _ptr(pos0))
+    _check(lib.kvq_append_quantize_multi(arr, len(items), _stream()))
 
 
 def kvq_append_norm_quantize(cache: KVCache, k: torch.Tensor, v: torch.Tensor, pos0: torch.Tensor,

@@ -521,6 +521,57 @@ KVQ_API kvq_status kvq_append_quantize(const kvq_cache* cache, const float* k, c
     return ok();
 }
 
+KVQ_API kvq_status kvq_append_quantize_multi(const kvq_append_item* items, int32_t n_items, hipStream_t stream)
+{
+    const char* what = "kvq_append_quantize_multi";
+    if (!items) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: items is NULL", what);
+    if (n_items < 1 || n_items > KVQ_MAX_SHARED_GROUPS)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: n_items %d outside [1, %d]", what, n_items,
+                    KVQ_MAX_SHARED_GROUPS);
+    kvq::AppendMulti P;
+    kvq::AppendParams bf[KVQ_MAX_SHARED_GROUPS];
+    int n_bf = 0;
+    int64_t blocks = 0;
+    P.n = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const kvq_append_item& it = items[i];
+        kvq_status st = check_cache(it.cache, what);
+        if (st != KVQ_OK) return st;
+        if (it.T < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: item %d: T %d < 0", what, i, it.T);
+        for (int j = 0; j < i; ++j)
+            if (items[j].cache->k_codes == it.cache->k_codes || items[j].cache->v_codes == it.cache->v_codes)
+                return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: items %d and %d write the same cache", what, j, i);
+        if (it.T == 0) continue;
+        kvq::AppendParams p;
+        int n_cand = 0;
+        st = append_params(it.cache, it.k, it.v, it.T, it.pos0, what, p, n_cand);
+        if (st != KVQ_OK) return st;
+        if (it.cache->k_bits == 16) {
+            bf[n_bf++] = p;
+            continue;
+        }
+        P.a[P.n] = p;
+        P.n_cand[P.n] = n_cand;
+        P.block_begin[P.n] = (int32_t)blocks;
+        blocks += (int64_t)n_cand * p.H * 2 * p.B;
+        if (blocks > INT_MAX) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: too many blocks in one launch", what);
+        ++P.n;
+    }
+    P.block_begin[P.n] = (int32_t)blocks;
+    if (trace_on())
+        fprintf(stderr, "[kvq] %s: %d quantized caches in %lld blocks, %d bf16 caches\n", what, P.n,
+                (long long)blocks, n_bf);
+    if (P.n > 0) {
+        const hipError_t e = kvq::launch_append_multi(P, stream);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    }
+    for (int i = 0; i < n_bf; ++i) {
+        const hipError_t e = kvq::launch_append_bf16(bf[i], stream);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    }
+    return ok();
+}
+
 KVQ_API kvq_status kvq_append_norm_quantize(const kvq_cache* cache, const float* k, const float* v,
                                             int32_t T, const int32_t* pos0, const float* k_weight, float eps,
                                             const float* rope_cos, const float* rope_sin, int32_t rope_dims,

@@ -22,6 +22,15 @@ struct AppendParams {
     int32_t n_written;    // tokens written per sequence
 };
 
+// Appends of several caches in one launch: cache i takes blocks
+// [block_begin[i], block_begin[i+1]), n_cand[i] x H x 2B of them.
+struct AppendMulti {
+    AppendParams a[KVQ_MAX_SHARED_GROUPS];
+    int32_t n_cand[KVQ_MAX_SHARED_GROUPS];
+    int32_t block_begin[KVQ_MAX_SHARED_GROUPS + 1];
+    int32_t n;
+};
+
 // The append with the keys' and values' norms and the keys' rotation in front.
 struct NormAppendParams {
     AppendParams a;
@@ -102,6 +111,7 @@ inline size_t part_floats(const AttnDesc& d)
 
 hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_append_bf16(const AppendParams& p, hipStream_t stream);
+hipError_t launch_append_multi(const AppendMulti& p, hipStream_t stream);
 hipError_t launch_append_norm(const NormAppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);

@@ -165,6 +165,28 @@ kvq_status kvq_append_quantize(const kvq_cache *cache,
                                hipStream_t stream);
 
 /*
+ * Several kvq_append_quantize calls in one launch, as one decode step writes
+ * the new token of every layer that owns a cache (page 80, gemma4/model.ts
+ * attentionTraining: appendWindow runs in each layer that owns its cache, and a
+ * KV-shared layer reads the donor's cache without appending).
+ *   items    n_items descriptors, 1 <= n_items <= KVQ_MAX_SHARED_GROUPS; item i
+ *            has the arguments of one kvq_append_quantize call (T may differ)
+ * Writes exactly what the separate calls would write.  Every item must name its
+ * own cache (no two items may share k_codes or v_codes: KVQ_ERR_INVALID_ARGUMENT).
+ * Quantized caches go in one kernel launch; a bf16 cache takes its own launch
+ * after it.  Items are checked in order; on an error nothing is launched.
+ */
+typedef struct {
+    const kvq_cache *cache;
+    const float *k, *v;     /* fp32 [B][H][T][D] of this cache */
+    int32_t T;
+    const int32_t *pos0;    /* int32 [B] */
+} kvq_append_item;
+
+kvq_status kvq_append_quantize_multi(const kvq_append_item *items, int32_t n_items,
+                                     hipStream_t stream);
+
+/*
  * kvq_append_quantize with the norms and the rotation in front, in one kernel
  * (page 80, gemma4/model.ts attentionTraining: keys through kNorm and then the
  * rotary embedding at their cache positions, values through vNorm, then

@@ -129,6 +129,29 @@ def test_append_validation(lib):
     assert f(ctypes.byref(cache(head_dim=96)), FAKE, FAKE, 4, FAKE, None) == 2
 
 
+def test_multi_append_validation(lib):
+    """Items are checked in order and nothing launches on an error, so every call
+    here returns before the HIP runtime is reached."""
+    a, b, c96 = cache(head_dim=128), cache(head_dim=256), cache(head_dim=96)
+    b.k_codes, b.v_codes = FAKE + 0x10000, FAKE + 0x20000
+    f = lib.kvq_append_quantize_multi
+
+    def items(*specs):
+        arr = (kvq.AppendItemStruct * max(1, len(specs)))()
+        for i, (c, T, k) in enumerate(specs):
+            arr[i] = kvq.AppendItemStruct(ctypes.pointer(c), k, FAKE, T, FAKE)
+        return arr
+    assert f(None, 1, None) == 1
+    assert f(items((a, 0, FAKE)), 0, None) == 1                     # n_items < 1
+    assert f(items(*[(a, 0, FAKE)] * 5), 5, None) == 1              # n_items > 4
+    assert f(items((a, 0, FAKE), (b, 0, FAKE)), 2, None) == 0        # nothing to write: no launch
+    assert f(items((a, 0, FAKE), (a, 0, FAKE)), 2, None) == 1        # one cache twice
+    assert f(items((a, 0, FAKE), (b, -1, FAKE)), 2, None) == 1       # T < 0
+    assert f(items((a, 4, FAKE), (b, 4, 0)), 2, None) == 1           # k NULL in the second item
+    assert f(items((a, 4, FAKE), (b, 4, FAKE + 4)), 2, None) == 1    # k not 16-byte aligned
+    assert f(items((a, 4, FAKE), (c96, 4, FAKE)), 2, None) == 2      # unsupported head_dim
+
+
 def test_normed_append_validation(lib):
     c = cache(head_dim=128)
     f = lib.kvq_append_norm_quantize

@@ -129,3 +129,71 @@ def test_append_golden_groups():
     for name, bits, x, codes, s, b in rows:       # and the oracle holds the hand values
         c, sb, bb = oracle.quantize_group(x, bits)
         assert (c == codes).all() and sb == s and bb == b, name
+
+
+# (D, k_bits, v_bits, R, batch, heads) of the caches one multi-append writes
+MULTI_CACHES = [(256, 4, 8, 64, 2, 2), (512, 8, 8, 48, 2, 1), (128, 16, 16, 64, 2, 2), (64, 4, 4, 32, 2, 3)]
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_append_multi_matches_oracle_and_single_calls(n):
+    """One launch over n caches of different head_dim, bits (bf16 among them),
+    capacity and T writes what n separate appends and the oracle write, call
+    after call, through ring wraps and a T > R call."""
+    specs = MULTI_CACHES[:n]
+    gm = [kvq.KVCache(B, H, D, kb, vb, R, window=R) for D, kb, vb, R, B, H in specs]
+    gs = [kvq.KVCache(B, H, D, kb, vb, R, window=R) for D, kb, vb, R, B, H in specs]
+    os_ = [oracle.Cache(B, H, D, R, kb, vb, window=R) for D, kb, vb, R, B, H in specs]
+    pos = [np.array([0, 5], np.int32) for _ in specs]
+    for step, Ts in enumerate([(1, 3, 1, 7), (37, 0, 70, 1), (1, 1, 1, 1), (5, 60, 2, 33)]):
+        items, dev = [], []
+        for i, (D, kb, vb, R, B, H) in enumerate(specs):
+            T = Ts[i]
+            k = small_randn(1000 * step + 10 * i, (B, H, T, D), D ** -0.25)
+            v = small_randn(1000 * step + 10 * i + 1, (B, H, T, D), D ** -0.25)
+            kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+            pd = torch.from_numpy(pos[i].copy()).cuda()
+            dev.append((kd, vd, pd))
+            items.append((gm[i], kd, vd, pd))
+            if T:
+                os_[i].append(k, v, pos[i])
+        print(f"multi append n={n} step={step} T={Ts[:n]}", flush=True)
+        kvq.kvq_append_quantize_multi(items)
+        for i in range(n):
+            kvq.kvq_append_quantize(gs[i], *dev[i])
+            pos[i] = pos[i] + Ts[i]
+        torch.cuda.synchronize()
+        for i in range(n):
+            assert_cache_equal(gm[i], os_[i])
+            for name in ("k_codes", "v_codes", "k_sb", "v_sb"):
+                a, b = getattr(gm[i], name), getattr(gs[i], name)
+                if a is not None:
+                    assert torch.equal(a, b), f"cache {i} {name} step {step}"
+
+
+def test_append_multi_workload_step():
+    """The decode step of the KV-shared workload at full size: every position but
+    the last appended one call at a time, then the last token of the donor
+    (D=256, 4/4-bit ring) and of the full layer (D=512, 8/8-bit) in one launch."""
+    wl = WORKLOADS["shared_decode_b32"]
+    print(f"multi append {wl.name}", flush=True)
+    sel = {c.name: [0, 7, 19, c.B - 1] for c in wl.caches}
+    gpu, orc, _, last = build_workload(wl, oracle_batches=sel, hold_last=True)
+    items = []
+    for spec in wl.caches:
+        k, v = last[spec.name]
+        pos0 = torch.full((spec.B,), spec.length - 1, dtype=torch.int32, device="cuda")
+        items.append((gpu[spec.name], k, v, pos0))
+    kvq.kvq_append_quantize_multi(items)
+    torch.cuda.synchronize()
+    for spec in wl.caches:
+        o, rows = orc[spec.name]
+        assert_cache_equal(gpu[spec.name], o, batches=rows)
+
+
+def test_append_multi_rejects_one_cache_twice():
+    g = kvq.KVCache(1, 1, 128, 4, 4, 32)
+    k = torch.zeros((1, 1, 1, 128), dtype=torch.float32, device="cuda")
+    pos0 = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_append_quantize_multi([(g, k, k, pos0), (g, k, k, pos0)])
