@@ -398,14 +398,24 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     };
 
-    // ---- QK of one step: partial S^T over this wave's groups into spart[par].
-    //      Tile t row r holds key 8*(r/4) + 4*t + r%4, so lane group lg ends with
-    //      keys 8*lg .. 8*lg+7.
-    auto qk = [&](const KRegs<D, KB>& kr, int par) {
+    // ---- Staging of a step's scale|bias words in this wave's LDS rows (the
+    //      words are read back by other lanes of the same wave after sync_wave).
+    auto stage_k = [&](const KRegs<D, KB>& kr) {
         if (sb_on) sm.ksb[wave][sb_g][sb_key] = kr.sb;
+    };
+    auto stage_v = [&](const VRegs<D, VB>& vr) {
+        if (sb_on) sm.vsb[wave][sb_g][sb_key] = vr.sb;
+    };
+    auto sync_wave = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // ---- QK of one step (its K words staged): partial S^T over this wave's
+    //      groups into spart[par].  Tile t row r holds key 8*(r/4) + 4*t + r%4,
+    //      so lane group lg ends with keys 8*lg .. 8*lg+7.
+    auto qk = [&](const KRegs<D, KB>& kr, int par) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int kk = 8 * (m >> 2) + 4 * t + (m & 3);
@@ -446,11 +456,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     };
 
-    // ---- full scores of one step (same in every wave, after the barrier) and the
-    //      online softmax in base 2; FULL: every key visible to every row.
-    auto softmax = [&](int st, int par, float (&p)[8], auto full_tag) {
+    // ---- full scores of one step (the same in every wave once the partials
+    //      met behind a barrier), in base 2, and their maximum over the row;
+    //      FULL: every key visible to every row.
+    auto scores = [&](int st, int par, float (&z)[8], auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        float z[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f32x4 sacc = sm.spart[par][0][t][lane];
@@ -469,7 +479,11 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         float mloc = z[0];
 #pragma unroll
         for (int k = 1; k < 8; ++k) mloc = fmaxf(mloc, z[k]);
-        const float mt = max_across_groups(mloc);
+        return max_across_groups(mloc);
+    };
+    // the online softmax in base 2: the running max moves (and O, corr and l
+    // are rescaled) only when a row's max grows by more than the slack
+    auto rescale = [&](float mt) {
         if (__any(mt > m_run + kRescaleSlack)) {
             const float m_new = fmaxf(m_run, mt);
             const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -479,6 +493,9 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             l_run *= alpha;
             m_run = m_new;
         }
+    };
+    auto probs = [&](const float (&z)[8], float (&p)[8], auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -487,6 +504,16 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             l_run += e;
             p[k] = FULL || z[k] != -INFINITY ? e : -1.0f;
         }
+    };
+
+    // fp16 operands hold p * s_v (p <= 2^8) and the V bias only while s_v < 2^7
+    // and |bias| < 2^15; a visible key beyond that sends this wave's step down
+    // the bf16 path, whose operands have fp32 range.
+    auto is_wide = [&](const VRegs<D, VB>& vr, int st) {
+        const int vkey = st + sb_key;
+        const bool big = sb_on && vkey >= j0 && vkey < j1 &&
+                         ((vr.sb & 0x7FFFu) >= 0x4300u || ((vr.sb >> 16) & 0x7FFFu) >= 0x4700u);
+        return __builtin_amdgcn_ballot_w64(big) != 0;
     };
 
     // ---- PV of one step with bf16 operands (any V scale and bias): every fp32
@@ -542,23 +569,14 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     };
 
-    // ---- PV of one step: O^T += V^T (P * s_v)^T per group; the bias term of all
-    //      groups in one MFMA.  Per-row visibility is carried by p (< 0: hidden);
-    //      kin: key inside the item's range, so its slot holds data (A side, where
-    //      a row is a quantization group and not a query row).
-    auto pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8], auto full_tag) {
+    // ---- PV of one step (its V words staged): O^T += V^T (P * s_v)^T per
+    //      group; the bias term of all groups in one MFMA.  Per-row visibility
+    //      is carried by p (< 0: hidden); kin: key inside the item's range, so
+    //      its slot holds data (A side, where a row is a quantization group and
+    //      not a query row).  WIDE: the step needs the bf16 operands.
+    auto pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8], auto full_tag, auto wide_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        if (sb_on) sm.vsb[wave][sb_g][sb_key] = vr.sb;
-        // fp16 operands hold p * s_v (p <= 2^8) and the V bias only while
-        // s_v < 2^7 and |bias| < 2^15; a visible key beyond that sends this
-        // wave's step down the bf16 path, whose operands have fp32 range.
-        const int vkey = st + sb_key;
-        const bool big = sb_on && vkey >= j0 && vkey < j1 &&
-                         ((vr.sb & 0x7FFFu) >= 0x4300u || ((vr.sb >> 16) & 0x7FFFu) >= 0x4700u);
-        const bool wide = __builtin_amdgcn_ballot_w64(big) != 0;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr bool WIDE = decltype(wide_tag)::value;
         bool kin[8];
         float pp[8];
 #pragma unroll
@@ -567,7 +585,7 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             kin[k] = FULL || (key >= j0 && key < j1);
             pp[k] = FULL ? p[k] : fmaxf(p[k], 0.0f);
         }
-        if (wide) {
+        if constexpr (WIDE) {
             pv_wide(vr, p, pp, kin, FULL);
             return;
         }
@@ -610,29 +628,22 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     };
 
     auto is_full = [&](int st) { return st >= full_lo && st + kStep - 1 <= full_hi; };
-    auto do_softmax = [&](int st, int par, float (&p)[8]) {
-        if (is_full(st)) softmax(st, par, p, std::true_type{});
-        else softmax(st, par, p, std::false_type{});
-    };
-    auto do_pv = [&](const VRegs<D, VB>& vr, int st, const float (&p)[8]) {
-        if (is_full(st)) pv(vr, st, p, std::true_type{});
-        else pv(vr, st, p, std::false_type{});
-    };
 
-    // Software pipeline over steps: iteration i runs QK of step i+1 and PV of
-    // step i (independent, so their MFMA and VALU chains interleave), then one
-    // barrier, then the softmax of step i+1.  K and V codes are loaded two
-    // steps ahead into ping-pong register sets (no copies: a copy would wait
-    // for the load); a V set is refilled right after its PV, so the first two
-    // steps of both go out with q and a two-step split waits for memory once.
-    // Loads are
-    // issued unconditionally with the step index clamped, so the wait counters
-    // stay exact; past the end the last step is read again from L2.
+    // Software pipeline over steps.  Step i runs, in one block of straight-line
+    // code: the scores of step i (its partials met behind the last barrier) and
+    // the softmax, QK of step i+1 (independent of them, so their LDS, MFMA and
+    // VALU latencies overlap), PV of step i; then one barrier.  Which code runs
+    // is chosen once per step: keys all visible or not (FULL), fp16 or bf16 PV
+    // operands (WIDE).  K and V codes are loaded two steps ahead into ping-pong
+    // register sets (no copies: a copy would wait for the load); a set is
+    // refilled right after its last use, so the first two steps of both go out
+    // with q and a two-step split waits for memory once.  Loads are issued
+    // unconditionally with the step index clamped, so the wait counters stay
+    // exact; past the end the last step is read again from L2.
     int last = max(nsteps - 1, 0);
     auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
     KRegs<D, KB> ka, kb;
     VRegs<D, VB> va, vb;
-    float p[8];
     // q and the first steps' codes go out together, before len[b] is known
     // (unconditional: a branch around loads would make every later wait a full one;
     // with no step the clamped index still names slots inside the cache)
@@ -655,27 +666,71 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         }
     }
     setup_q();
+
+    // step i with a step after it: kq holds step i+1's K words, kl is refilled
+    // with step i+2's, vr holds step i's V words and is refilled with step i+2's
+    auto step = [&](int i, int par, const KRegs<D, KB>& kq, KRegs<D, KB>& kl, VRegs<D, VB>& vr, auto full_tag,
+                    auto wide_tag) {
+        const int st = st0 + i * kStep;
+        stage_k(kq);
+        stage_v(vr);
+        sync_wave();
+        load_k(kl, stp(i + 2));
+        float z[8], p[8];
+        const float mt = scores(st, par, z, full_tag);
+        rescale(mt);
+        probs(z, p, full_tag);
+        qk(kq, par ^ 1);
+        pv(vr, st, p, full_tag, wide_tag);
+        load_v(vr, stp(i + 2));
+        __syncthreads();
+    };
+    auto run_step = [&](int i, int par, const KRegs<D, KB>& kq, KRegs<D, KB>& kl, VRegs<D, VB>& vr) {
+        const int st = st0 + i * kStep;
+        const bool wide = is_wide(vr, st);
+        if (is_full(st)) {
+            if (wide) step(i, par, kq, kl, vr, std::true_type{}, std::true_type{});
+            else step(i, par, kq, kl, vr, std::true_type{}, std::false_type{});
+        } else {
+            if (wide) step(i, par, kq, kl, vr, std::false_type{}, std::true_type{});
+            else step(i, par, kq, kl, vr, std::false_type{}, std::false_type{});
+        }
+    };
+    // the last step: its softmax and PV only
+    auto last_step = [&](int i, int par, const VRegs<D, VB>& vr) {
+        const int st = st0 + i * kStep;
+        const bool wide = is_wide(vr, st);
+        stage_v(vr);
+        sync_wave();
+        float z[8], p[8];
+        auto tail = [&](auto full_tag) {
+            const float mt = scores(st, par, z, full_tag);
+            rescale(mt);
+            probs(z, p, full_tag);
+            if (wide) pv(vr, st, p, full_tag, std::true_type{});
+            else pv(vr, st, p, full_tag, std::false_type{});
+        };
+        if (is_full(st)) tail(std::true_type{});
+        else tail(std::false_type{});
+    };
+
     if (nsteps > 0) {
+        stage_k(ka);
+        sync_wave();
         qk(ka, 0);
         __syncthreads();
-        do_softmax(st0, 0, p);
     }
     for (int i = 0; i < nsteps; i += 2) {
-        load_k(ka, stp(i + 2));
-        if (i + 1 < nsteps) qk(kb, 1);
-        do_pv(va, st0 + i * kStep, p);
-        load_v(va, stp(i + 2));
-        __syncthreads();
-        if (i + 1 >= nsteps) break;
-        do_softmax(st0 + (i + 1) * kStep, 1, p);
-
-        load_k(kb, stp(i + 3));
-        if (i + 2 < nsteps) qk(ka, 0);
-        do_pv(vb, st0 + (i + 1) * kStep, p);
-        load_v(vb, stp(i + 3));
-        __syncthreads();
-        if (i + 2 >= nsteps) break;
-        do_softmax(st0 + (i + 2) * kStep, 0, p);
+        if (i + 1 >= nsteps) {
+            last_step(i, 0, va);
+            break;
+        }
+        run_step(i, 0, kb, ka, va);
+        if (i + 2 >= nsteps) {
+            last_step(i + 1, 1, vb);
+            break;
+        }
+        run_step(i + 1, 1, ka, kb, vb);
     }
 
     // ---- fold the bias term into O: lane (m, lg) holds corr[group row 4*lg+i][query row m]

@@ -128,18 +128,28 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Reductions across the four 16-lane row groups (lanes l, l^16, l^32, l^48).
+// Reductions across the four 16-lane row groups (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap permutes: v_permlane16_swap(v, v) leaves lane l
+// holding v_l and v_(l^16) in its two results, v_permlane32_swap(v, v) v_l
+// and v_(l^32).  VALU only, no LDS round trip.  The pairs are combined as
+// (l, l^16) first, then (l, l^32): every lane of the four gets the same value.
+__device__ __forceinline__ float max_with_l16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float max_across_groups(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    v = max_with_l16(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_groups(float v)
 {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
