@@ -363,9 +363,13 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
 
     int nsteps = j0 < j1 ? ((j1 - 1) >> 5) - (j0 >> 5) + 1 : 0;
     int st0 = j0 & ~(kStep - 1);
+    // step i of the item (clamped to its last step)
+    int last = max(nsteps - 1, 0);
+    auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
     const int64_t kslot0 = (int64_t)bh * R;
     const uint32_t* __restrict__ kcodes = as_global(P.k_codes) + kslot0 * KW;
-    const uint32_t* __restrict__ vcodes = as_global(P.v_codes) + ((int64_t)bh * (R / 8) * D + 64 * g0 + m) * VW;
+    const uint32_t* __restrict__ vcodes = as_global(P.v_codes) + (int64_t)bh * (R / 8) * D * VW;
+    const int vlane = (64 * g0 + m) * VW;          // this lane's column within a V block
     // lane -> (key, group) of the scale|bias word it stages each step
     const int sb_key = GPW == 2 ? lane >> 1 : lane & 31;
     const int sb_g = GPW == 2 ? lane & 1 : 0;
@@ -373,8 +377,8 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     const uint32_t* __restrict__ ksbp = as_global(P.k_sb) + kslot0 * G + g0 + sb_g;
     const uint32_t* __restrict__ vsbp = as_global(P.v_sb) + kslot0 * G + g0 + sb_g;
 
-    auto load_k = [&](KRegs<D, KB>& r, int st) {
-        const int st_mod = st % R;
+    auto load_k = [&](KRegs<D, KB>& r, int i) {
+        const int st_mod = stp(i) % R;
         r.sb = ksbp[sb_on ? wrap_slot(st_mod + sb_key, R) * G : 0];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -387,10 +391,10 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
             }
         }
     };
-    auto load_v = [&](VRegs<D, VB>& r, int st) {
-        const int st_mod = st % R;
+    auto load_v = [&](VRegs<D, VB>& r, int i) {
+        const int st_mod = stp(i) % R;
         r.sb = vsbp[sb_on ? wrap_slot(st_mod + sb_key, R) * G : 0];
-        const uint32_t* vrow = vcodes + (wrap_slot(st_mod + 8 * lg, R) >> 3) * (D * VW);
+        const uint32_t* vrow = vcodes + ((int64_t)(wrap_slot(st_mod + 8 * lg, R) >> 3) * (D * VW) + vlane);
 #pragma unroll
         for (int dd = 0; dd < DTW; ++dd) {
             if constexpr (VB == 8) r.vc[dd] = *reinterpret_cast<const u32x2*>(vrow + 16 * dd * VW);
@@ -640,18 +644,16 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
     // with q and a two-step split waits for memory once.  Loads are issued
     // unconditionally with the step index clamped, so the wait counters stay
     // exact; past the end the last step is read again from L2.
-    int last = max(nsteps - 1, 0);
-    auto stp = [&](int i) { return st0 + min(i, last) * kStep; };
     KRegs<D, KB> ka, kb;
     VRegs<D, VB> va, vb;
     // q and the first steps' codes go out together, before len[b] is known
     // (unconditional: a branch around loads would make every later wait a full one;
     // with no step the clamped index still names slots inside the cache)
     load_q();
-    load_k(ka, stp(0));
-    load_v(va, stp(0));
-    load_k(kb, stp(1));
-    load_v(vb, stp(1));
+    load_k(ka, 0);
+    load_v(va, 0);
+    load_k(kb, 1);
+    load_v(vb, 1);
     const int len_act = min(max(__builtin_amdgcn_readfirstlane(len_lane), 0), P.max_len);
     if (len_act != P.max_len) {
         ranges(len_act);
@@ -659,10 +661,10 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         st0 = j0 & ~(kStep - 1);
         last = max(nsteps - 1, 0);
         if (nsteps > 0) {
-            load_k(ka, stp(0));
-            load_v(va, stp(0));
-            load_k(kb, stp(1));
-            load_v(vb, stp(1));
+            load_k(ka, 0);
+            load_v(va, 0);
+            load_k(kb, 1);
+            load_v(vb, 1);
         }
     }
     setup_q();
@@ -675,14 +677,14 @@ __device__ __forceinline__ void attn_body(const AttnDesc& P, int idx, AttnSmem<D
         stage_k(kq);
         stage_v(vr);
         sync_wave();
-        load_k(kl, stp(i + 2));
+        load_k(kl, i + 2);
         float z[8], p[8];
         const float mt = scores(st, par, z, full_tag);
         rescale(mt);
         probs(z, p, full_tag);
         qk(kq, par ^ 1);
         pv(vr, st, p, full_tag, wide_tag);
-        load_v(vr, stp(i + 2));
+        load_v(vr, i + 2);
         __syncthreads();
     };
     auto run_step = [&](int i, int par, const KRegs<D, KB>& kq, KRegs<D, KB>& kl, VRegs<D, VB>& vr) {

@@ -99,6 +99,10 @@ kvq_status check_cache(const kvq_cache* c, const char* what)
         return fail(KVQ_ERR_CAPACITY, "%s: window %d exceeds capacity %d", what, c->window, c->capacity);
     if (c->capacity > (INT_MAX / 2))
         return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d too large", what, c->capacity);
+    // the kernels address one (sequence, KV head)'s codes with 32-bit word offsets
+    if ((int64_t)c->capacity * c->head_dim * std::max(c->k_bits, c->v_bits) / 32 > INT_MAX)
+        return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity %d x head_dim %d at %d bits exceeds 8 GiB of codes per "
+                    "sequence and KV head", what, c->capacity, c->head_dim, std::max(c->k_bits, c->v_bits));
     return KVQ_OK;
 }
 

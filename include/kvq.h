@@ -125,7 +125,9 @@ typedef enum {
  *
  * Requirements: group_size == 64; head_dim a multiple of 64 from 64 to 512 (a bf16
  * cache: a multiple of 128); k_bits, v_bits in {4, 8}, or both 16; capacity a
- * multiple of 8 and at least KVQ_MIN_CAPACITY; 0 <= window <= capacity (0: full).
+ * multiple of 8 and at least KVQ_MIN_CAPACITY, with capacity * head_dim *
+ * max(k_bits, v_bits) / 8 at most 8 GiB (the codes of one sequence and KV head
+ * are addressed with 32-bit word offsets); 0 <= window <= capacity (0: full).
  * Chunk reads of more than 16 rows per KV head have kernels of their own at
  * head_dim 256 and 512 (the model's); at the other head_dims every read runs on
  * the decode kernel, which reads the keys once per 16-row tile.

@@ -73,7 +73,8 @@ def decode(lib, c, Hq=8, max_len=4096, scale=1.0, ws=0, q=FAKE, out=FAKE, ln=FAK
     (dict(head_dim=100), 2), (dict(head_dim=576), 2), (dict(head_dim=32), 2), (dict(group_size=32), 2),
     (dict(k_bits=16, v_bits=16, head_dim=320), 2), (dict(k_bits=5), 2),
     (dict(v_bits=2), 2), (dict(capacity=12), 1), (dict(capacity=0), 1), (dict(window=1024), 3),
-    (dict(window=-1), 1), (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(k_codes=0), 1),
+    (dict(window=-1), 1), (dict(capacity=1 << 24, window=0, head_dim=512, k_bits=8, v_bits=8), 1),
+    (dict(capacity=1 << 23, window=0, head_dim=512, k_bits=16, v_bits=16), 1), (dict(batch=0), 1), (dict(n_kv_heads=0), 1), (dict(k_codes=0), 1),
     (dict(v_sb=0), 1), (dict(capacity=24, window=0), 1), (dict(k_bits=16), 2), (dict(v_bits=16), 2),
     (dict(k_bits=16, v_bits=16, v_codes=0), 1), (dict(k_codes=FAKE + 8), 1), (dict(v_sb=FAKE + 4), 1),
     (dict(batch=40000), 1), (dict(n_kv_heads=70000), 1),
