@@ -2,10 +2,11 @@
 """Benchmark of quantized-KV attention on one MI355X.
 
 A step is one pass of the hot path over one batch of the workload: the step's
-new token(s) are quantized and appended to the cache (kvq_append_quantize, one
-kvq_append_quantize_multi launch for workloads with several caches, or the
-fused kvq_decode_step on decode workloads), then the read runs
-(kvq_attn_decode / kvq_attn_prefill_chunk / kvq_attn_decode_shared /
+new token(s) are quantized and appended to the cache and the read runs.  Decode
+workloads take the fused step (kvq_decode_step; kvq_decode_step_shared for the
+KV-shared groups), which does both in one read launch; prefill, verify and
+mixed workloads append (kvq_append_quantize, or one kvq_append_quantize_multi
+launch for several caches) and then read (kvq_attn_prefill_chunk /
 kvq_attn_mixed).  Inputs are resident in HBM before timing starts.
 
 To read HBM rather than the 256 MB last-level cache, every timed step reads one
@@ -202,11 +203,9 @@ class Runner:
             k, v = self.step_kv["kv"]
             self.step_k1 = k.reshape(spec.B, spec.Hkv, spec.D)
             self.step_v1 = v.reshape(spec.B, spec.Hkv, spec.D)
-        # single-cache decode steps run as one fused call (append + read); the
-        # others as two (for the KV-shared groups, kvq_decode_step_shared measured
-        # 144 us against 130 us for the appends + kvq_attn_decode_shared: its new
-        # token's split makes the unsplit donor read go through the combine)
-        self.fused = wl.kind == "decode"
+        # decode steps (one cache or KV-shared groups) run as one fused call
+        # (append + read); prefill, verify and mixed reads as append, then read
+        self.fused = wl.kind in ("decode", "shared")
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 

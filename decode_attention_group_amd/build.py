@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["append.hip", "append_norm.hip", "attn.hip", "prefill.hip", "prefill_q.hip", "prefill_codes.hip", "bf16_cache.hip",
+SOURCES = ["append.hip", "append_norm.hip", "attn.hip", "attn_step.hip", "prefill.hip", "prefill_q.hip", "prefill_codes.hip", "bf16_cache.hip",
            "kvq_api.hip"]
 # measurement probes (include/kvq_probes.h), a library of their own
 PROBE_LIB = os.path.join(HERE, "libkvq_probes.so")

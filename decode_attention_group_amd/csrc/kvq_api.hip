@@ -162,8 +162,9 @@ kvq_status check_read(const ReadSpec& r, const char* what)
 }
 
 // Fill the descriptor's shape and split plan.  `target_wg` is the number of
-// workgroups this read should aim for.
-void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
+// workgroups this read should aim for.  fold: a fused step's token (quantized
+// cache) is taken by the last split of each item instead of a split of its own.
+void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d, bool fold = false)
 {
     const kvq_cache* c = r.cache;
     std::memset(&d, 0, sizeof(d));
@@ -200,7 +201,11 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     const int64_t steps = (vis + 2 * kvq::kStep - 1) / kvq::kStep;
     const int64_t items = (int64_t)d.B * d.Hkv * d.n_rt;
     int64_t S = (target_wg + items - 1) / items;
-    if (r.k_new) S = std::max<int64_t>(1, S - 1);     // the new token's split counts against the target
+    // a fused step's token: a split of its own per item (it counts against the
+    // target), unless the last split takes it (fold)
+    const bool tok_fold = r.k_new && fold && c->k_bits != 16;
+    const bool tok_split = r.k_new && !tok_fold;
+    if (tok_split) S = std::max<int64_t>(1, S - 1);
     // two steps per split where that still leaves 128 workgroups: a workgroup's
     // first step costs a full memory round trip, its second overlaps it
     // (measured on 8 sequences x 2 KV heads over a 512-key window: 11.3 us at 9
@@ -209,8 +214,7 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
     const int forced = env_splits();
     if (forced > 0) S = forced;
-    // a fused step adds one split per item for the new token
-    const int64_t max_s = r.k_new ? kvq::kMaxSplits - 1 : kvq::kMaxSplits;
+    const int64_t max_s = tok_split ? kvq::kMaxSplits - 1 : kvq::kMaxSplits;
     S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(steps, max_s)));
     const int64_t steps_per = (steps + S - 1) / S;
     d.split_len = (int)(steps_per * kvq::kStep);
@@ -219,7 +223,8 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d)
         d.k_new = r.k_new;
         d.v_new = r.v_new;
         d.excl = 1;
-        d.S += 1;
+        d.tok_fold = tok_fold ? 1 : 0;
+        if (tok_split) d.S += 1;
     }
     d.n_items = (int)(items * d.S);
 }
@@ -316,6 +321,13 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
     // the others in proportion to their bytes, so that the launch stays within
     // what the chip holds at once (a second wave of workgroups would start the
     // longest items late).
+    // A fused step's token takes a split of its own when its read launches alone
+    // (the token's work runs beside the other splits); with several reads in the
+    // launch the last split of each item takes it, so an unsplit read (a sliding
+    // donor) stays without partials and a combine.
+    int n_shared = 0;
+    for (int i = 0; i < n; ++i) n_shared += own[i] ? 0 : 1;
+    const bool fold = n_shared > 1;
     int fixed_wg = 0;
     double free_bytes = 0.0;
     bool fixed[KVQ_MAX_SHARED_GROUPS];
@@ -324,9 +336,9 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         if (own[i]) continue;
         const kvq_cache* c = rs[i].cache;
         const int rows = (rs[i].C == 1 ? rs[i].n_layers : rs[i].C) * (rs[i].Hq / c->n_kv_heads);
-        // (a fused step's read takes one more workgroup per item, for the new token)
+        // (a fused step's token as a split of its own takes one more workgroup per item)
         const int64_t items = (int64_t)c->batch * c->n_kv_heads * ((rows + kvq::kRowTile - 1) / kvq::kRowTile) *
-                              (rs[i].k_new ? 2 : 1);
+                              (rs[i].k_new && !(fold && c->k_bits != 16) ? 2 : 1);
         fixed[i] = total > 0 && items >= kTargetWg * (bytes[i] / total);
         if (fixed[i]) fixed_wg += (int)std::min<int64_t>(items, kTargetWg);
         else free_bytes += bytes[i];
@@ -343,7 +355,7 @@ size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)
         } else {
             const double share = fixed[i] ? 0.0 : (free_bytes > 0 ? bytes[i] / free_bytes : 1.0);
             const int target = std::max(1, (int)std::lround(free_wg * share));
-            plan_read(rs[i], target, d);
+            plan_read(rs[i], target, d, fold);
             d.item_begin = total_items;
             total_items += d.n_items;
         }
@@ -389,8 +401,9 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
         big &= kvq::chunk_kernels_for(Ps.d[i].D) && !kvq::cfg_is_bf16(Ps.d[i].cfg);
     }
     auto launch_one = [&](const kvq::AttnParams& p, int items) {
-        return kvq::cfg_is_bf16(p.d[0].cfg) ? kvq::launch_attn_bf16(p, items, stream)
-                                            : kvq::launch_attn(p, items, false, stream);
+        if (kvq::cfg_is_bf16(p.d[0].cfg)) return kvq::launch_attn_bf16(p, items, stream);
+        if (p.n_desc == 1 && p.d[0].k_new && !p.d[0].tok_fold) return kvq::launch_attn_step(p, items, stream);
+        return kvq::launch_attn(p, items, false, stream);
     };
     if (trace_on())
         for (int i = 0; i < n; ++i)
@@ -405,8 +418,7 @@ kvq_status run_reads(const ReadSpec* rs, int n, void* workspace, size_t workspac
     } else if (same) {
         e = launch_one(Ps, total_items);
     } else if (big) {
-        e = kvq::launch_new_tokens(Ps, stream);   // (fused steps only)
-        if (e == hipSuccess) e = kvq::launch_attn(Ps, total_items, true, stream);
+        e = kvq::launch_attn(Ps, total_items, true, stream);
     } else {
         // Mixed configurations outside the fused set: one launch per descriptor.
         for (int i = 0; i < Ps.n_desc && e == hipSuccess; ++i) {

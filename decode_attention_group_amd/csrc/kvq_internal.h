@@ -63,7 +63,10 @@ struct AttnDesc {
     const int32_t* len;
     const float* k_new;     // fused decode step: the step's fp32 K and V rows [B][Hkv][D]
     const float* v_new;     //   (null otherwise); split S-1 of every item takes that token
+                            //   (see tok_fold)
     int32_t excl;           // 1: the attention splits leave out position len-1 (fused step)
+    int32_t tok_fold;       // fused step on a quantized cache: 1 the last split takes the
+                            //   token after its keys (no extra split), 0 a split of its own
     float* part;            // split partials (null when S == 1)
     uint16_t* band;         // prefill: dequantized band tiles, bf16 [B][Hkv][nk/32][64*D] (the
                             // LDS image of each 32-key step: K rows, then V^T rows, swizzled);
@@ -115,9 +118,9 @@ hipError_t launch_append_multi(const AppendMulti& p, hipStream_t stream);
 hipError_t launch_append_norm(const NormAppendParams& p, int n_cand, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStream_t stream);
+// the fused decode step of one descriptor (its k_new set)
+hipError_t launch_attn_step(const AttnParams& p, int total_items, hipStream_t stream);
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
-// The new-token splits of fused-step descriptors read by launch_attn(..., multi=true).
-hipError_t launch_new_tokens(const AttnParams& p, hipStream_t stream);
 // The chunk's band tiles (dequantized, or a bf16 copy) when the prefill kernel
 // needs them; then the prefill kernel itself.
 hipError_t launch_band(const AttnParams& p, hipStream_t stream);

@@ -157,16 +157,30 @@ SHARED_STEP_GROUPS = [
 ]
 
 
-@pytest.mark.parametrize("n_groups", [2, 4])
-def test_decode_step_shared_small(n_groups):
+# groups of one configuration (one launch of the same kernel), the first with
+# 24 rows per KV head (two row tiles, both taking the token; tile 0 writes it)
+SHARED_SAME_CONFIG = [
+    (2, 256, 4, 4, 512, 300, 3, 16),
+    (2, 256, 4, 4, 1024, 0, 1, 8),
+]
+
+
+@pytest.mark.parametrize("groups", [SHARED_STEP_GROUPS[:1], SHARED_STEP_GROUPS[:2], SHARED_STEP_GROUPS[:3],
+                                    SHARED_STEP_GROUPS, SHARED_SAME_CONFIG],
+                         ids=["1", "2", "3", "4", "same-config"])
+def test_decode_step_shared_small(groups):
     """Each group's cache equals kvq_append_quantize's for the same token; every
     layer's output is within tolerance of the oracle after the oracle's append.
-    Ragged lengths: the second sequence is one position behind."""
+    Ragged lengths: the second sequence is one position behind.  One group
+    launches alone (the token a split of its own); several groups share a launch
+    (the last split of each item takes the token), of two configurations, of
+    one, or per read where a configuration has no shared kernel."""
+    n_groups = len(groups)
     B, L = 2, 600
     lens_np = np.array([L + 1, L], np.int32)
     lens = torch.from_numpy(lens_np).cuda()
-    groups, refs, caches, ks, vs = [], [], [], [], []
-    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(SHARED_STEP_GROUPS[:n_groups]):
+    groups_, refs, caches, ks, vs = [], [], [], [], []
+    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(groups):
         g, o = history(B, Hkv, D, kb, vb, R, W, L, seed=500 + 10 * gi)
         k = small_randn(600 + gi, (B, Hkv, D), D ** -0.25)
         v = small_randn(700 + gi, (B, Hkv, D), D ** -0.25)
@@ -175,13 +189,13 @@ def test_decode_step_shared_small(n_groups):
         kvq.kvq_append_quantize(ref_cache, kd[:, :, None].contiguous(), vd[:, :, None].contiguous(), lens - 1)
         o.append(k[:, :, None], v[:, :, None], lens_np - 1)
         qs = [small_q_bits(800 + 10 * gi + l, (B, Hq, 1, D), D ** -0.25) for l in range(layers)]
-        groups.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens, L + 1))
+        groups_.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens, L + 1))
         refs.append([o.attend(x, lens_np)[:, :, 0] for x in qs])
         caches.append((g, ref_cache))
         ks.append(kd)
         vs.append(vd)
-    print(f"shared decode step, {n_groups} groups", flush=True)
-    outs = kvq.kvq_decode_step_shared(groups, ks, vs)
+    print(f"shared decode step, {n_groups} groups {groups}", flush=True)
+    outs = kvq.kvq_decode_step_shared(groups_, ks, vs)
     torch.cuda.synchronize()
     for gi, (g, ref_cache) in enumerate(caches):
         assert_same_cache(g, ref_cache, f"group {gi}")
