@@ -413,3 +413,31 @@ def test_minimum_capacity_ring(bits):
     out2 = kvq.kvq_attn_prefill_chunk(g2, q_dev(qc), torch.from_numpy(lens2).cuda(), 77)
     torch.cuda.synchronize()
     assert_close(torch_bf16_to_f64(out2), o2.attend(qc, lens2), f"chunk R=32 W=16 bits={bits}")
+
+
+def test_shared_many_small_items():
+    """A small donor read with many work items (16 sequences x 4 KV heads,
+    window 64, three layers) beside a large full-layer read in one launch (the
+    donor's items need no split, the full layer's many).  Outputs against the
+    oracle, ragged lengths; also as kvq_attn_mixed."""
+    B, L = 16, 2000
+    lens_np = np.array([L - (b % 3) for b in range(B)], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    g, o = make_pair(B, 4, 256, 4, 4, 64, 64, L, seed=120)
+    g2, o2 = make_pair(B, 1, 512, 8, 8, 2048, 0, L, seed=121)
+    qa = [small_q_bits(130 + i, (B, 16, 1, 256), 0.25) for i in range(3)]
+    qb = [small_q_bits(140, (B, 8, 1, 512), 0.21)]
+    print("shared, many small items", flush=True)
+    outs = kvq.kvq_attn_decode_shared([kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qa], lens, L),
+                                       kvq.SharedGroup(g2, [q_dev(qb[0][:, :, 0].copy())], lens, L)])
+    reads = [kvq.Read(g, [q_dev(x.copy()) for x in qa], lens, L),
+             kvq.Read(g2, [q_dev(qb[0].copy())], lens, L)]
+    outs_m = kvq.kvq_attn_mixed(reads)
+    torch.cuda.synchronize()
+    for i in range(3):
+        ref = o.attend(qa[i], lens_np)[:, :, 0]
+        assert_close(torch_bf16_to_f64(outs[0][i]), ref, f"donor layer {i}")
+        assert_close(torch_bf16_to_f64(outs_m[0][i])[:, :, 0], ref, f"mixed donor layer {i}")
+    ref = o2.attend(qb[0], lens_np)[:, :, 0]
+    assert_close(torch_bf16_to_f64(outs[1][0]), ref, "full layer")
+    assert_close(torch_bf16_to_f64(outs_m[1][0])[:, :, 0], ref, "mixed full layer")

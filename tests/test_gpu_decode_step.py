@@ -203,6 +203,40 @@ def test_decode_step_shared_small(groups):
             assert_close(torch_bf16_to_f64(outs[gi][l]), ref, f"group {gi} layer {l}")
 
 
+def test_decode_step_shared_many_small_items():
+    """The fused step over a small donor read with many items (16 sequences x 4
+    KV heads, window 64, three layers) and a large full layer: both take their
+    token in their last split (the donor's only one).  Caches word for word
+    against the plain append, outputs against the oracle, ragged lengths (the
+    donor's tokens rewrite ring slots)."""
+    B, L = 16, 1999
+    lens_np = np.array([L + 1 - (b % 3) for b in range(B)], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    specs = [(4, 256, 4, 4, 64, 64, 3, 16), (1, 512, 8, 8, 2048, 0, 1, 8)]
+    groups, refs, caches, ks, vs = [], [], [], [], []
+    for gi, (Hkv, D, kb, vb, R, W, layers, Hq) in enumerate(specs):
+        g, o = history(B, Hkv, D, kb, vb, R, W, L, seed=1500 + 10 * gi)
+        k = small_randn(1600 + gi, (B, Hkv, D), D ** -0.25)
+        v = small_randn(1700 + gi, (B, Hkv, D), D ** -0.25)
+        ref_cache = clone_cache(g)
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        kvq.kvq_append_quantize(ref_cache, kd[:, :, None].contiguous(), vd[:, :, None].contiguous(), lens - 1)
+        o.append(k[:, :, None], v[:, :, None], lens_np - 1)
+        qs = [small_q_bits(1800 + 10 * gi + l, (B, Hq, 1, D), D ** -0.25) for l in range(layers)]
+        groups.append(kvq.SharedGroup(g, [q_dev(x[:, :, 0].copy()) for x in qs], lens, L + 1))
+        refs.append([o.attend(x, lens_np)[:, :, 0] for x in qs])
+        caches.append((g, ref_cache))
+        ks.append(kd)
+        vs.append(vd)
+    print("shared decode step, many small items", flush=True)
+    outs = kvq.kvq_decode_step_shared(groups, ks, vs)
+    torch.cuda.synchronize()
+    for gi, (g, ref_cache) in enumerate(caches):
+        assert_same_cache(g, ref_cache, f"group {gi}")
+        for l, ref in enumerate(refs[gi]):
+            assert_close(torch_bf16_to_f64(outs[gi][l]), ref, f"group {gi} layer {l}")
+
+
 def test_decode_step_shared_matches_two_calls():
     """Against appends followed by kvq_attn_decode_shared on copies of the caches:
     the same caches word for word, outputs within the attention tolerance."""
