@@ -134,8 +134,7 @@ hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStre
     if (multi) {
         for (int i = 0; i < p.n_desc; ++i)
             if (p.d[i].k_new != nullptr && !p.d[i].tok_fold) return hipErrorInvalidValue;
-        attn_kernel_multi<<<grid, dim3(256), 0, stream>>>(p);
-        return hipGetLastError();
+        return launch_read(attn_kernel_multi, grid, dim3(256), p, stream);
     }
     // one descriptor without a token: the plain kernel; otherwise the kernel that
     // takes folded tokens (a token as a split of its own launches from attn_step.hip)
@@ -145,9 +144,8 @@ hipError_t launch_attn(const AttnParams& p, int total_items, bool multi, hipStre
     switch (p.d[0].cfg) {
 #define KVQ_CASE(D_, KB_, VB_) \
     case cfg_of(D_, KB_, VB_): \
-        if (plain) attn_kernel<D_, KB_, VB_, true, kTokNone><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
-        else attn_kernel<D_, KB_, VB_, false, kTokFold><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
-        break;
+        return plain ? launch_read(attn_kernel<D_, KB_, VB_, true, kTokNone>, grid, dim3(64 * Shape<D_>::NW), p, stream) \
+                     : launch_read(attn_kernel<D_, KB_, VB_, false, kTokFold>, grid, dim3(64 * Shape<D_>::NW), p, stream);
 #define KVQ_D(D_) KVQ_CASE(D_, 4, 4) KVQ_CASE(D_, 4, 8) KVQ_CASE(D_, 8, 4) KVQ_CASE(D_, 8, 8)
     KVQ_D(64) KVQ_D(128) KVQ_D(192) KVQ_D(256) KVQ_D(320) KVQ_D(384) KVQ_D(448) KVQ_D(512)
 #undef KVQ_D

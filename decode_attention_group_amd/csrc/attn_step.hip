@@ -14,8 +14,7 @@ hipError_t launch_attn_step(const AttnParams& p, int total_items, hipStream_t st
     switch (p.d[0].cfg) {
 #define KVQ_CASE(D_, KB_, VB_) \
     case cfg_of(D_, KB_, VB_): \
-        attn_kernel<D_, KB_, VB_, true, kTokSplit><<<grid, dim3(64 * Shape<D_>::NW), 0, stream>>>(p); \
-        break;
+        return launch_read(attn_kernel<D_, KB_, VB_, true, kTokSplit>, grid, dim3(64 * Shape<D_>::NW), p, stream);
 #define KVQ_D(D_) KVQ_CASE(D_, 4, 4) KVQ_CASE(D_, 4, 8) KVQ_CASE(D_, 8, 4) KVQ_CASE(D_, 8, 8)
     KVQ_D(64) KVQ_D(128) KVQ_D(192) KVQ_D(256) KVQ_D(320) KVQ_D(384) KVQ_D(448) KVQ_D(512)
 #undef KVQ_D

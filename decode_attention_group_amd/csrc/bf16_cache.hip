@@ -366,13 +366,12 @@ hipError_t launch_attn_bf16(const AttnParams& p, int total_items, hipStream_t st
 {
     const dim3 grid(total_items), block(256);
     switch (p.d[0].D) {
-    case 128: attn_bf16_kernel<128><<<grid, block, 0, stream>>>(p); break;
-    case 384: attn_bf16_kernel<384><<<grid, block, 0, stream>>>(p); break;
-    case 256: attn_bf16_kernel<256><<<grid, block, 0, stream>>>(p); break;
-    case 512: attn_bf16_kernel<512><<<grid, block, 0, stream>>>(p); break;
+    case 128: return launch_read(attn_bf16_kernel<128>, grid, block, p, stream);
+    case 384: return launch_read(attn_bf16_kernel<384>, grid, block, p, stream);
+    case 256: return launch_read(attn_bf16_kernel<256>, grid, block, p, stream);
+    case 512: return launch_read(attn_bf16_kernel<512>, grid, block, p, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -27,20 +27,22 @@ thread_local char g_err[512] = "";
 thread_local hipEvent_t g_mark_before = nullptr;
 thread_local hipEvent_t g_mark_after = nullptr;
 
-void mark_before(hipStream_t stream)
+// armed between mark_before and mark_after: the events the read kernels take
+thread_local hipEvent_t g_kstart = nullptr;
+thread_local hipEvent_t g_kstop = nullptr;
+
+void mark_before(hipStream_t)
 {
-    if (g_mark_before) (void)hipEventRecord(g_mark_before, stream);
+    g_kstart = g_mark_before;
+    g_kstop = g_mark_after;
     g_mark_before = nullptr;
 }
 
-void mark_after(hipStream_t stream)
-{
-    if (g_mark_after) (void)hipEventRecord(g_mark_after, stream);
-}
+void mark_after(hipStream_t) { g_kstart = g_kstop = nullptr; }
 
 // Every attention call ends its marks (armed for one call only).
 struct MarkScope {
-    ~MarkScope() { g_mark_before = g_mark_after = nullptr; }
+    ~MarkScope() { g_mark_before = g_mark_after = g_kstart = g_kstop = nullptr; }
 };
 
 kvq_status fail(kvq_status st, const char* fmt, ...)
@@ -471,6 +473,16 @@ kvq_status static_scratch(void** ptr, const char* what)
 }
 
 }  // namespace
+
+namespace kvq {
+bool read_marks(hipEvent_t& start, hipEvent_t& stop)
+{
+    start = g_kstart;
+    stop = g_kstop;
+    g_kstart = nullptr;
+    return start != nullptr || stop != nullptr;
+}
+}  // namespace kvq
 
 KVQ_API const char* kvq_last_error(void) { return g_err; }
 

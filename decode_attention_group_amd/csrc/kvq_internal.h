@@ -1,6 +1,7 @@
 // Launch parameter blocks shared by the host API and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,6 +111,23 @@ inline size_t part_floats(const AttnDesc& d)
     if (d.S <= 1) return 0;
     const size_t items = (size_t)d.B * d.Hkv * d.n_rt * d.S * kRowTile;
     return items * (size_t)d.D + items * 2;
+}
+
+// Measurement marks (kvq_mark_next_read).  While a call's marks are armed, its
+// read kernels launch with the start event attached to the first and the stop
+// event to each (the last one stands), on the kernels themselves
+// (hipExtLaunchKernel): the pair brackets their execution, not the dispatch gaps
+// around them.  read_marks hands out the armed events (the start once).
+bool read_marks(hipEvent_t& start, hipEvent_t& stop);
+
+template <class K>
+hipError_t launch_read(K kernel, dim3 grid, dim3 block, const AttnParams& p, hipStream_t stream)
+{
+    void* args[] = {const_cast<AttnParams*>(&p)};
+    hipEvent_t start = nullptr, stop = nullptr;
+    if (read_marks(start, stop))
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream, start, stop, 0);
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
 }
 
 hipError_t launch_append(const AppendParams& p, int n_cand, hipStream_t stream);

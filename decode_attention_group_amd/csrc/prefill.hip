@@ -552,15 +552,16 @@ hipError_t launch_prefill(const AttnParams& p, int total_items, hipStream_t stre
     const bool direct = cfg_is_bf16(d.cfg) && d.band == nullptr;
     const dim3 grid(total_items);
     if (d.D == 256) {
-        if (direct) prefill_kernel<256, true><<<grid, dim3(64 * pf_waves<256>()), 0, stream>>>(p);
-        else prefill_kernel<256, false><<<grid, dim3(64 * pf_waves<256>()), 0, stream>>>(p);
-    } else if (d.D == 512) {
-        if (direct) prefill_kernel<512, true><<<grid, dim3(64 * pf_waves<512>()), 0, stream>>>(p);
-        else prefill_kernel<512, false><<<grid, dim3(64 * pf_waves<512>()), 0, stream>>>(p);
-    } else {
-        return hipErrorInvalidValue;
+        const dim3 block(64 * pf_waves<256>());
+        return direct ? launch_read(prefill_kernel<256, true>, grid, block, p, stream)
+                      : launch_read(prefill_kernel<256, false>, grid, block, p, stream);
     }
-    return hipGetLastError();
+    if (d.D == 512) {
+        const dim3 block(64 * pf_waves<512>());
+        return direct ? launch_read(prefill_kernel<512, true>, grid, block, p, stream)
+                      : launch_read(prefill_kernel<512, false>, grid, block, p, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

@@ -432,7 +432,7 @@ hipError_t launch_prefill_codes(const AttnParams& p, int total_items, hipStream_
     switch (p.d[0].cfg) {
 #define KVQ_CP(D_, KB_, VB_) \
     case cfg_of(D_, KB_, VB_): \
-        codes_prefill_kernel<D_, KB_, VB_><<<grid, dim3(CpShape<D_>::NT), 0, stream>>>(p); break;
+        return launch_read(codes_prefill_kernel<D_, KB_, VB_>, grid, dim3(CpShape<D_>::NT), p, stream);
     KVQ_CP(256, 4, 4) KVQ_CP(256, 4, 8) KVQ_CP(256, 8, 4) KVQ_CP(256, 8, 8)
     KVQ_CP(512, 4, 4) KVQ_CP(512, 4, 8) KVQ_CP(512, 8, 4) KVQ_CP(512, 8, 8)
 #undef KVQ_CP

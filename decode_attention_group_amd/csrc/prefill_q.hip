@@ -535,7 +535,7 @@ hipError_t launch_qprefill(const AttnParams& p, int total_items, hipStream_t str
     const dim3 grid(total_items), block(64 * kQpWaves);
     switch (p.d[0].cfg) {
 #define KVQ_QP(D_, KB_, VB_) \
-    case cfg_of(D_, KB_, VB_): qprefill_kernel<D_, KB_, VB_><<<grid, block, 0, stream>>>(p); break;
+    case cfg_of(D_, KB_, VB_): return launch_read(qprefill_kernel<D_, KB_, VB_>, grid, block, p, stream);
     KVQ_QP(256, 4, 4) KVQ_QP(256, 4, 8) KVQ_QP(256, 8, 4) KVQ_QP(256, 8, 8)
     KVQ_QP(512, 4, 4) KVQ_QP(512, 4, 8) KVQ_QP(512, 8, 4) KVQ_QP(512, 8, 8)
 #undef KVQ_QP
