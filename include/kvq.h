@@ -432,13 +432,15 @@ size_t kvq_prefill_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads,
 /*
  * (host) Measurement: arm two events for the next attention call made on this
  * thread (kvq_attn_decode, kvq_decode_step, kvq_attn_prefill_chunk,
- * kvq_attn_decode_shared or kvq_attn_mixed).  That call records `before` on its
- * stream just before it launches its main kernel (the split read, the prefill
- * kernel or the short-chunk kernel: not a band copy and not the combine of the
- * split partials) and `after` just after it, so hipEventElapsedTime(before,
- * after) is the main kernel's time on the stream.  Either event may be NULL.
- * The marks are used by that one call, whether or not it launches anything, and
- * then dropped.  Events are caller-created; nothing else changes.
+ * kvq_attn_decode_shared or kvq_attn_mixed).  That call attaches `before` to
+ * the start of its first read kernel (the split read, the prefill kernel or the
+ * short-chunk kernel: not an append, a band copy or the combine of the split
+ * partials) and `after` to the end of each read kernel it launches (the last
+ * one stands), on the kernels themselves, so hipEventElapsedTime(before, after)
+ * is the time from the first read kernel's start to the last one's end, without
+ * the dispatch gaps around them.  Either event may be NULL.  The marks are used
+ * by that one call and then dropped; a call that fails before its launch
+ * records neither event.  Events are caller-created; nothing else changes.
  */
 kvq_status kvq_mark_next_read(hipEvent_t before, hipEvent_t after);
 
