@@ -84,12 +84,16 @@ struct QpSmem {
             float ks[kQpWaves][2][32];        // [wave][group][key]: K scales of the wave's current step
             _Float16 vs[kQpWaves][2][32];     // [wave][group][slot]: V scales (fp16, MFMA slot order)
             _Float16 vb[kQpWaves][2][32];     // [wave][group][slot]: V biases
-            f32x4 spart[2][kQpWaves][4][64];  // partial S^T [step parity][wave][quad][lane]
+            union {
+                f32x4 spart[2][kQpWaves][4][64];  // partial S^T [step parity][wave][quad][lane]
+                u32x4 qs[kQpRows][D / 8 + 1];     // before the loop: the item's q rows (16-byte
+                                                  // chunks, one pad chunk per row)
+            };
             f16x8 qf[NS][2][4][64];           // q operands [slice][group][part][lane]
         } loop;
         struct {
-            f32x4 o[(NKG - 1) * NS][QpShape<D>::NDT][4][64];  // O^T tiles of the key groups past the first
-            float ml[(NKG - 1) * NS][2][32];                 // their (m, l) per row
+            f32x4 o[kQpWaves][QpShape<D>::NDT][4][64];  // every wave's O^T tiles
+            float ml[kQpWaves][2][32];                 // and its (m, l) per row
         } merge;
     };
 };
@@ -154,14 +158,23 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     };
     ranges(P.max_len);
 
-    // ---- q of this row and slice: B operands of the 16 QK MFMAs (group g, part j:
-    //      slot 8h+e holds column c0 + 64g + 32h + 8j + order(e)), and the group sums
-    const uint16_t* qrow = as_global(P.q[0]) + (((int64_t)b * P.Hq + hq) * C + qi) * D + c0 + 32 * h;
-    u32x4 qraw[2][4];
+    // ---- q of the item's rows, loaded with a row's 16-byte chunks on consecutive
+    //      lanes (rows past the last are zero); staged in LDS below
+    constexpr int QCH = D / 8;                          // 16-byte chunks per row
+    constexpr int QLD = kQpRows * QCH / (64 * kQpWaves);  // chunks per thread
+    static_assert(QLD * 64 * kQpWaves == kQpRows * QCH, "q chunks per thread");
+    u32x4 qld[QLD];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qraw[g][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * g + 8 * j);
+    for (int k = 0; k < QLD; ++k) {
+        const int c = tid + 64 * kQpWaves * k;
+        const int gr = row0 + c / QCH;
+        qld[k] = (u32x4)0;
+        if (gr < P.n_rows) {
+            const int qk = gr / P.hpk, hk = hkv * P.hpk + gr % P.hpk;
+            qld[k] = *reinterpret_cast<const u32x4*>(as_global(P.q[0]) + (((int64_t)b * P.Hq + hk) * C + qk) * D +
+                                                     8 * (c % QCH));
+        }
+    }
 
     // ---- per-step register sets: K codes of this lane's key (32 columns of each
     //      of the slice's 2 groups), its K scale|bias words, V code words of this
@@ -229,6 +242,21 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
             load(rb, stp(1));
         }
     }
+
+    // ---- q of this row and slice from LDS: B operands of the 16 QK MFMAs (group g,
+    //      part j: slot 8h+e holds column c0 + 64g + 32h + 8j + order(e)), and the
+    //      group sums
+#pragma unroll
+    for (int k = 0; k < QLD; ++k) {
+        const int c = tid + 64 * kQpWaves * k;
+        sm.loop.qs[c / QCH][c % QCH] = qld[k];
+    }
+    __syncthreads();
+    u32x4 qraw[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qraw[g][j] = sm.loop.qs[li][(c0 + 64 * g + 32 * h + 8 * j) / 8];
 
     // q: power of 2 per row and slice, fp16 operands (to LDS), group sums in three
     // bf16 parts
@@ -458,58 +486,64 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     }
     float L = l_run + __shfl_xor(l_run, 32);
 
-    // ---- merge the key groups: groups past the first leave (O, m, l) in LDS
+    // ---- merge the key groups: every wave leaves (O, m, l) in LDS; wave (kg, ds)
+    //      then merges column tiles kg*TPW .. kg*TPW+TPW-1 of slice ds over the
+    //      groups and writes them
+    constexpr int TPW = NDT / NKG;
+    static_assert(TPW * NKG == NDT, "column tiles per wave");
+    __syncthreads();                           // the loop's LDS is free
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            sm.merge.o[wave][dt][q4][lane] = (f32x4){O[dt][4 * q4], O[dt][4 * q4 + 1], O[dt][4 * q4 + 2],
+                                                     O[dt][4 * q4 + 3]};
+    if (h == 0) {
+        sm.merge.ml[wave][0][li] = m_run;
+        sm.merge.ml[wave][1][li] = L;
+    }
     __syncthreads();
-    if constexpr (NKG > 1) {
-        if (kg > 0) {
-            const int k = (kg - 1) * NS + ds;
+    float mk[NKG], wk[NKG];
+    float mx = -INFINITY;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+    for (int k1 = 0; k1 < NKG; ++k1) {
+        mk[k1] = sm.merge.ml[k1 * NS + ds][0][li];
+        mx = fmaxf(mx, mk[k1]);
+    }
+    float Lm = 0.0f;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    sm.merge.o[k][dt][q4][lane] = (f32x4){O[dt][4 * q4], O[dt][4 * q4 + 1], O[dt][4 * q4 + 2],
-                                                          O[dt][4 * q4 + 3]};
-            if (h == 0) {
-                sm.merge.ml[k][0][li] = m_run;
-                sm.merge.ml[k][1][li] = L;
+    for (int k1 = 0; k1 < NKG; ++k1) {
+        wk[k1] = mk[k1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk[k1] - mx);   // empty groups: 0
+        Lm += wk[k1] * sm.merge.ml[k1 * NS + ds][1][li];
+    }
+    f32x16 Om[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        Om[t] = (f32x16){};
+#pragma unroll
+        for (int k1 = 0; k1 < NKG; ++k1)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 v = sm.merge.o[k1 * NS + ds][kg * TPW + t][q4][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Om[t][4 * q4 + i] += wk[k1] * v[i];
             }
-        }
-        __syncthreads();
-        if (kg > 0) return;
-#pragma unroll
-        for (int k1 = 1; k1 < NKG; ++k1) {
-            const int k = (k1 - 1) * NS + ds;
-            const float mo = sm.merge.ml[k][0][li], lo = sm.merge.ml[k][1][li];
-            const float mn = fmaxf(m_run, mo);
-            if (mn == -INFINITY) continue;
-            const float a0 = __builtin_amdgcn_exp2f(m_run - mn), a1 = __builtin_amdgcn_exp2f(mo - mn);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 t = sm.merge.o[k][dt][q4][lane];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) O[dt][4 * q4 + i] = O[dt][4 * q4 + i] * a0 + t[i] * a1;
-                }
-            L = L * a0 + lo * a1;
-            m_run = mn;
-        }
     }
     if (!row_ok) return;
 
     // ---- write: lane (li, h) holds columns c0 + 32 dt + 8 (v/4) + 4h + v%4 of row li
     if (S == 1) {
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float inv = Lm > 0.0f ? 1.0f / Lm : 0.0f;
         uint16_t* orow = as_global(P.out[0]) + (((int64_t)b * P.Hq + hq) * C + qi) * D + c0 + 4 * h;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x16& o = Om[t];
                 uint2 w;
-                w.x = f32_to_bf16_rne(O[dt][4 * q4] * inv) | ((uint32_t)f32_to_bf16_rne(O[dt][4 * q4 + 1] * inv) << 16);
-                w.y = f32_to_bf16_rne(O[dt][4 * q4 + 2] * inv) |
-                      ((uint32_t)f32_to_bf16_rne(O[dt][4 * q4 + 3] * inv) << 16);
-                *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) = w;
+                w.x = f32_to_bf16_rne(o[4 * q4] * inv) | ((uint32_t)f32_to_bf16_rne(o[4 * q4 + 1] * inv) << 16);
+                w.y = f32_to_bf16_rne(o[4 * q4 + 2] * inv) | ((uint32_t)f32_to_bf16_rne(o[4 * q4 + 3] * inv) << 16);
+                *reinterpret_cast<uint2*>(orow + 32 * (kg * TPW + t) + 8 * q4) = w;
             }
         return;
     }
@@ -518,15 +552,15 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     const int64_t prow = (((int64_t)bh * P.n_rt + rt16) * S + s) * kRowTile + r16;
     float* po = as_global(P.part) + prow * D + c0 + 4 * h;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * q4) =
-                (f32x4){O[dt][4 * q4], O[dt][4 * q4 + 1], O[dt][4 * q4 + 2], O[dt][4 * q4 + 3]};
-    if (ds == 0 && h == 0) {
+            *reinterpret_cast<f32x4*>(po + 32 * (kg * TPW + t) + 8 * q4) =
+                (f32x4){Om[t][4 * q4], Om[t][4 * q4 + 1], Om[t][4 * q4 + 2], Om[t][4 * q4 + 3]};
+    if (wave == 0 && h == 0) {
         float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
-        pml[0] = m_run;
-        pml[1] = L;
+        pml[0] = mx;
+        pml[1] = Lm;
     }
 }
 
