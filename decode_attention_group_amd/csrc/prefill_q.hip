@@ -90,6 +90,7 @@ struct QpSmem {
                                                   // chunks, one pad chunk per row)
             };
             f16x8 qf[NS][2][4][64];           // q operands [slice][group][part][lane]
+            int done[kQpWaves];               // per wave: steps whose partial scores are in spart
         } loop;
         struct {
             f32x4 o[kQpWaves][QpShape<D>::NDT][4][64];  // every wave's O^T tiles
@@ -328,6 +329,7 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
         qb = __builtin_bit_cast(bf16x8, w);
     }
 
+    if (lane == 0) sm.loop.done[wave] = 0;
     __syncthreads();                           // the q operands are in LDS
     f32x16 O[NDT];
 #pragma unroll
@@ -337,11 +339,27 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
 
     // ---- one step: QK (partial over the slice), exchange (NS == 2), softmax, PV.
     //      full: every key of the step is visible to every row (no masks)
-    auto step = [&](const Regs& r, int st, int par, bool active, bool full) {
-        if (!active) {                         // this key group has no step here (uniform per group)
-            __syncthreads();                   // the exchange barrier the other groups take
-            return;
+    // The partial scores of a step meet only within a key group (its NS waves), so
+    // the exchange waits on the group's waves alone: each wave publishes its count
+    // of steps whose partials are in LDS and waits for its partners' counts to
+    // reach the same step.  Key groups then drift apart, and the two waves on a
+    // SIMD (different key groups) overlap one's MFMAs with the other's VALU work.
+    // The partials are double-buffered (step parity): a wave overwrites its
+    // buffer two steps later only after its partners published the step in
+    // between, which they do after reading it.  Every wave of a group runs the
+    // same steps (the step count depends on the group alone).
+    auto exchange_wait = [&](int n) {
+        if (lane == 0) __hip_atomic_store(&sm.loop.done[wave], n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int o = 1; o < NS; ++o) {
+            const int w = kg * NS + (ds + o) % NS;
+            while (__hip_atomic_load(&sm.loop.done[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+                __builtin_amdgcn_s_sleep(1);
         }
+    };
+    auto step = [&](const Regs& r, int st, int i, bool active, bool full) {
+        if (!active) return;                   // this key group has no step here (uniform per group)
+        const int par = i & 1;
         // stage this step's K scales (fp32) and V scales and biases (fp16, in the
         // slot order of the PV operands; keys outside the item's range, which may
         // sit in slots no append wrote, as 0); lane (li, h) holds key qp_key(li)'s
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             sm.loop.spart[par][wave][q4][lane] = (f32x4){z[4 * q4], z[4 * q4 + 1], z[4 * q4 + 2], z[4 * q4 + 3]};
-        __syncthreads();
+        exchange_wait(i + 1);
 #pragma unroll
         for (int o = 1; o < NS; ++o)
 #pragma unroll
@@ -466,7 +484,7 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     auto is_full = [&](int st) { return st >= full_lo && st + kStep - 1 <= full_hi; };
     auto do_step = [&](const Regs& r, int i) {
         const int st = stp(i);
-        step(r, st, i & 1, i < n_my, is_full(st));
+        step(r, st, i, i < n_my, is_full(st));
     };
     for (int i = 0; i < n_all; i += 2) {
         do_step(ra, i);
