@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     const AttnDesc& P = Pp.d[0];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave: uniform (scalar)
     const int li = lane & 31, h = lane >> 5;
     const int ds = wave % NS, kg = wave / NS;  // head_dim slice, key group
     const int c0 = ds * 128;                   // first column of the slice
