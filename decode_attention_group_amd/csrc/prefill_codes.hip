@@ -147,7 +147,14 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
     const uint32_t* __restrict__ vcodes = as_global(P.v_codes) + (int64_t)bh * (R / 8) * D * VW;
 
     // ---- loads of one step into registers
-    const int k_key = tid / Sh::KCH, k_chunk = tid % Sh::KCH;   // K dequant assignment
+    // K dequant assignment: lane l of a 32-lane half writes LDS row l (MFMA order,
+    // below), i.e. key 8*((l/4)%4) + 4*(l/16) + l%4, chunk tid/32: the 16 lanes of
+    // one LDS write pass write 16 consecutive rows, whose 4-bank row offsets keep
+    // them on distinct banks
+    const int k_row = tid & 31;
+    const int k_key = (((k_row >> 2) & 3) << 3) | (((k_row >> 4) & 1) << 2) | (k_row & 3);
+    const int k_chunk = tid >> 5;
+    static_assert(Sh::KCH * kStep == NT, "one K chunk per thread");
     auto load_codes = [&](Codes& c, int st) {
         const int st_mod = st % R;
         const uint32_t* krow = kcodes + wrap_slot(st_mod + k_key, R) * KW + k_chunk * Codes::KWT;
@@ -205,8 +212,7 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
             const uint32_t sw = sm.ks[slot][g][k_key], bw = sm.kb[slot][g][k_key];
             const f16x2 s2 = __builtin_bit_cast(f16x2, sw | (sw << 16));
             const f16x2 b2 = __builtin_bit_cast(f16x2, bw | (bw << 16));
-            const int krow = 16 * ((k_key >> 2) & 1) + 4 * (k_key >> 3) + (k_key & 3);
-            _Float16* dst = &sm.kh[slot][krow][k_chunk * Sh::CH];
+            _Float16* dst = &sm.kh[slot][k_row][k_chunk * Sh::CH];   // row k_row holds key k_key
 #pragma unroll
             for (int w = 0; w < Codes::KWT; w += (KB == 8 ? 2 : 1)) {
                 f16x2 pr[4];
