@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void attn_kernel_multi(AttnParams P)
 // are 16 column quads x 16 split lanes.  Each split lane issues the loads of all
 // its splits first, then folds them with a running max, so the partials are
 // read in one round trip; the 16 lanes' results meet in LDS.  Splits that saw
-// no key (m_s = -inf) contribute nothing.
+// no key (m_s = -inf) contribute nothing.  A descriptor with part_h holds o_s / l_s
+// as fp16, which is multiplied back by l_s.
 constexpr int kCombCols = 64;
 constexpr int kCombLanes = 16;
 constexpr int kCombMaxPer = kMaxSplits / kCombLanes;
@@ -82,7 +83,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P)
             const float2 ml = *reinterpret_cast<const float2*>(msrc + (int64_t)s * kRowTile * 2);
             ms[j] = ml.x;
             ls[j] = ml.y;
-            os[j] = *reinterpret_cast<const f32x4*>(src + s * sstride);
+            if (d.part_h) {                    // o / l as fp16: back to o
+                const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po) +
+                                                                (((int64_t)ib * S + s) * kRowTile + r) * D + col);
+                const f16x2 lo = __builtin_bit_cast(f16x2, w.x), hi = __builtin_bit_cast(f16x2, w.y);
+                os[j] = (f32x4){(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]} * ml.y;
+            } else {
+                os[j] = *reinterpret_cast<const f32x4*>(src + s * sstride);
+            }
         } else {
             ms[j] = -INFINITY;
             ls[j] = 0.0f;

@@ -294,6 +294,7 @@ void plan_codes_desc(const ReadSpec& r, kvq::AttnDesc& d)
     d.S = (int)((steps + steps_per - 1) / steps_per);
     d.n_items = (int)(items * d.S);
     d.own_launch = 1;
+    d.part_h = 1;
 }
 
 size_t plan_all(const ReadSpec* rs, int n, kvq::AttnParams& P, int& total_items)

@@ -85,6 +85,8 @@ struct AttnDesc {
     int32_t cfg;            // kernel configuration id (head_dim, k_bits, v_bits)
     int32_t own_launch;     // host: a short chunk of a mixed launch, read by the codes
                             // kernel in a launch of its own (items counted from 0)
+    int32_t part_h;         // split partials of o hold o / l as fp16 (the short-chunk kernel,
+                            // whose V values are fp16 already); else o as fp32
 };
 
 struct AttnParams {
@@ -104,8 +106,9 @@ inline bool cfg_is_bf16(int cfg) { return cfg >= 32; }
 // launch exist for the model's head_dims; every other read takes the decode kernel.
 inline bool chunk_kernels_for(int D) { return D == 256 || D == 512; }
 
-// Partial buffer of one descriptor: o [B*Hkv*n_rt][S][16][D] fp32, then
-// (m, l) [B*Hkv*n_rt][S][16][2] fp32.
+// Partial buffer of one descriptor: o [B*Hkv*n_rt][S][16][D] fp32 (or o / l as
+// fp16 in the first half of that space, part_h), then (m, l) [B*Hkv*n_rt][S][16][2]
+// fp32.
 inline size_t part_floats(const AttnDesc& d)
 {
     if (d.S <= 1) return 0;

@@ -412,11 +412,18 @@ __device__ __forceinline__ void codes_body(const AttnDesc& P, int idx, CpSmem<D>
             *reinterpret_cast<uint2*>(orow + dcol + 16 * dt) = w;
         }
     } else {
+        // o / l as fp16 (part_h): a convex combination of this kernel's fp16 V values
         const int64_t ib = (int64_t)bh * P.n_rt + rt;
         const int64_t prow = (ib * S + s) * kRowTile + m;
-        float* po = as_global(P.part) + prow * D;
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        uint16_t* po = reinterpret_cast<uint16_t*>(as_global(P.part)) + prow * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dcol + 16 * dt) = O[dt];
+        for (int dt = 0; dt < DT; ++dt) {
+            const f32x4 o = O[dt] * inv;
+            const f16x2 lo = {(_Float16)o[0], (_Float16)o[1]}, hi = {(_Float16)o[2], (_Float16)o[3]};
+            *reinterpret_cast<uint2*>(po + dcol + 16 * dt) =
+                (uint2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
         if (lg == 0 && dh == 0) {
             float* pml = as_global(P.part) + (size_t)P.B * P.Hkv * P.n_rt * S * kRowTile * D + prow * 2;
             pml[0] = m_run;

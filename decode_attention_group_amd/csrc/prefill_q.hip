@@ -123,8 +123,8 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     const int idx = xcd_item(blockIdx.x, gridDim.x);
     const int S = P.S;
     const int n_rt32 = (P.n_rows + kQpRows - 1) / kQpRows;
-    const int s = idx % S;
-    const int rt = (idx / S) % n_rt32;
+    const int rt = idx % n_rt32;               // row items of one split side by side (one XCD's L2)
+    const int s = (idx / n_rt32) % S;
     const int bh = idx / (S * n_rt32);
     const int b = bh / P.Hkv, hkv = bh - b * P.Hkv;
     const int R = P.R, W = P.W, C = P.C;
