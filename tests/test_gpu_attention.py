@@ -386,6 +386,33 @@ def test_mixed_decode_and_verify_reads(extra):
             assert_close(torch_bf16_to_f64(outs[i][l]), ref, f"read {i} layer {l}")
 
 
+def test_mixed_with_chunk_in_its_own_launch():
+    """A verify chunk long enough for the short-chunk kernel (40 rows over more
+    than 2048 keys) beside decode reads: the chunk runs in a launch of its own,
+    the decode reads share the other launch, one combine serves both; against
+    the oracle, ragged lengths, two calls in a row."""
+    B, L = 2, 3000
+    lens_np = np.array([L, L - 11], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    specs = [  # Hkv, D, kb, vb, R, W, layers, Hq, chunk
+        (2, 256, 4, 8, 520, 512, 3, 8, 1),
+        (1, 512, 8, 8, 4096, 0, 1, 8, 5),
+    ]
+    reads, refs = [], []
+    for i, (Hkv, D, kb, vb, R, W, layers, Hq, C) in enumerate(specs):
+        g, o = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=420 + 10 * i)
+        qs = [small_q_bits(520 + 10 * i + l, (B, Hq, C, D), D ** -0.25) for l in range(layers)]
+        reads.append(kvq.Read(g, [q_dev(x) for x in qs], lens, L))
+        refs.append([o.attend(x, lens_np) for x in qs])
+    print("mixed with an own-launch chunk", flush=True)
+    for rep in range(2):
+        outs = kvq.kvq_attn_mixed(reads)
+        torch.cuda.synchronize()
+        for i in range(len(specs)):
+            for l, ref in enumerate(refs[i]):
+                assert_close(torch_bf16_to_f64(outs[i][l]), ref, f"call {rep} read {i} layer {l}")
+
+
 def test_mixed_rejects_multi_layer_chunk():
     g = kvq.KVCache(1, 1, 256, 4, 4, 64)
     q = torch.zeros(1, 8, 2, 256, dtype=torch.bfloat16, device="cuda")

@@ -97,3 +97,42 @@ def test_graph_replays_of_prefill(bits):
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
         kvq.kvq_attn_prefill_chunk(g, q, lens, L, workspace=ws)             # eager work in between
         torch.cuda.synchronize()
+
+
+def test_graph_replays_of_mixed_read():
+    """A mixed read whose verify chunk runs in a launch of its own (three kernel
+    launches: the decode reads, the short-chunk kernel, the combine)."""
+    B, L = 2, 3000
+    lens = torch.tensor([L, L - 7], dtype=torch.int32, device="cuda")
+    specs = [(2, 256, 4, 8, 520, 512, 3, 8, 1), (1, 512, 8, 8, 4096, 0, 1, 8, 5)]
+    reads = []
+    for i, (Hkv, D, kb, vb, R, W, layers, Hq, C) in enumerate(specs):
+        g, _ = make_pair(B, Hkv, D, kb, vb, R, W, L, seed=621 + i)
+        qs = [q_dev(small_q_bits(622 + 10 * i + l, (B, Hq, C, D), D ** -0.25)) for l in range(layers)]
+        reads.append(kvq.Read(g, qs, lens, L))
+    print("graph mixed read", flush=True)
+    ws = torch.empty(max(kvq.kvq_mixed_workspace_bytes(reads), 256), dtype=torch.uint8, device="cuda")
+    refs = [[x.clone() for x in o] for o in kvq.kvq_attn_mixed(reads, workspace=ws)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kvq.kvq_attn_mixed(reads, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kvq.kvq_attn_mixed(reads, workspace=ws)
+    for rep in range(4):
+        for r in reads:
+            for o in r.out:
+                o.fill_(float("nan"))
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, r in enumerate(reads):
+            for l, o in enumerate(r.out):
+                assert torch.equal(o.view(torch.int16), refs[i][l].view(torch.int16)), f"replay {rep} read {i}.{l}"
+        kvq.kvq_attn_mixed(reads, workspace=ws)                             # eager work in between
+        torch.cuda.synchronize()
