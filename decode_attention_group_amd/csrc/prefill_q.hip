@@ -64,6 +64,7 @@ __device__ __forceinline__ constexpr int qp_slot4(int t) { return (t & 1) * 4 + 
 
 constexpr int kQpRows = kQprefillRows;      // query rows per work item
 constexpr float kQpRescaleSlack = 8.0f;
+constexpr int kQpSpinLimit = 1 << 20;      // polls of a partner's step count before giving up
 
 constexpr int kQpWaves = 8;
 
@@ -348,12 +349,17 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     // buffer two steps later only after its partners published the step in
     // between, which they do after reading it.  Every wave of a group runs the
     // same steps (the step count depends on the group alone).
+    // The wait is bounded (kQpSpinLimit polls of about 64 clocks, tens of
+    // milliseconds): the partners reach every step of their group, so the bound
+    // is never met; it only guarantees that every wave exits.
     auto exchange_wait = [&](int n) {
         if (lane == 0) __hip_atomic_store(&sm.loop.done[wave], n, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
         for (int o = 1; o < NS; ++o) {
             const int w = kg * NS + (ds + o) % NS;
-            while (__hip_atomic_load(&sm.loop.done[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n)
+            for (int spin = 0; spin < kQpSpinLimit &&
+                               __hip_atomic_load(&sm.loop.done[w], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n;
+                 ++spin)
                 __builtin_amdgcn_s_sleep(1);
         }
     };
