@@ -21,7 +21,7 @@
 // Codes and scale|bias words are fetched two and three steps ahead; LDS holds
 // two steps; one barrier per step.  Rows follow the decode layout
 // (row = query * (Hq/Hkv) + head), so split partials go through the decode
-// combine kernel.
+// combine kernel (as o / l in fp16: this kernel's V values are fp16 already).
 #include <type_traits>
 
 #include "kvq_device.h"
