@@ -338,8 +338,8 @@ __global__ __launch_bounds__(64 * kQpWaves) void qprefill_kernel(AttnParams Pp)
     f32x16 corr = (f32x16){};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // ---- one step: QK (partial over the slice), exchange (NS == 2), softmax, PV.
-    //      full: every key of the step is visible to every row (no masks)
+    // ---- one step: QK (partial over the slice), exchange within the key group,
+    //      softmax, PV.  full: every key of the step is visible to every row (no masks)
     // The partial scores of a step meet only within a key group (its NS waves), so
     // the exchange waits on the group's waves alone: each wave publishes its count
     // of steps whose partials are in LDS and waits for its partners' counts to
