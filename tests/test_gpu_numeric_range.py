@@ -108,11 +108,14 @@ def test_shared_launch_with_large_values_and_queries():
             check(out, o.attend(x, ln, scale=1.0 / qfac)[:, :, 0], vfac, "shared")
 
 
+@pytest.mark.parametrize("vexp", [12, 14])
 @pytest.mark.parametrize("kb,vb", [(8, 8), (4, 8), (16, 16)])
-def test_chunk_kernels_inside_their_range(kb, vb):
-    """The short-chunk kernel (8 queries: 64 rows over 2600 keys) with q times 2^17 and
-    V times 2^12, and the band path (96 queries) with the same inputs."""
-    vfac, qfac = 2.0 ** 12, 2.0 ** 17
+def test_chunk_kernels_inside_their_range(kb, vb, vexp):
+    """The short-chunk kernel (8 queries: 64 rows over 2600 keys, 128 splits whose
+    partials hold o / l in fp16) with q times 2^17 and V times 2^12 or 2^14 (values
+    to about 1.3e4, inside its 2^15 bound), and the band path (96 queries) with the
+    same inputs."""
+    vfac, qfac = 2.0 ** vexp, 2.0 ** 17
     B, Hq, H, D, L = 2, 8, 1, 512, 2600
     k = small_randn(4301, (B, H, L, D), 0.21)
     v = small_randn(4302, (B, H, L, D), 0.21) * np.float32(vfac)
@@ -120,7 +123,7 @@ def test_chunk_kernels_inside_their_range(kb, vb):
     lens = np.full(B, L, np.int32)
     for C in (8, 96):
         qc = scaled_q(4303 + C, (B, Hq, C, D), 0.21, qfac)
-        print(f"chunk C={C} K{kb}/V{vb}", flush=True)
+        print(f"chunk C={C} K{kb}/V{vb} V x 2^{vexp}", flush=True)
         out = kvq.kvq_attn_prefill_chunk(g, q_dev(qc), torch.from_numpy(lens).cuda(), L, scale=1.0 / qfac)
         torch.cuda.synchronize()
         check(out, o.attend(qc, lens, scale=1.0 / qfac), vfac, f"chunk C={C} K{kb}/V{vb}")
