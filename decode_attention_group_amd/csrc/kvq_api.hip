@@ -214,6 +214,12 @@ void plan_read(const ReadSpec& r, int target_wg, kvq::AttnDesc& d, bool fold = f
     // splits against 11.7 us at 18); below that, one step per split
     const int64_t min_steps_per_split = items * ((steps + 1) / 2) >= 128 ? 2 : 1;
     S = std::min<int64_t>(S, (steps + min_steps_per_split - 1) / min_steps_per_split);
+    // a short read (a window of up to 32 steps) in about 192 workgroups at most:
+    // past that, more splits cost more in partials and in the combine than their
+    // parallel first loads gain (5 queries x 8 heads of B8 over a 512-key window,
+    // 32 items: 13.7 us at 6 splits against 14.8 us at 9; the sliding decode, 16
+    // items, sits on its plateau at 9-12 splits)
+    if (steps <= 32) S = std::min<int64_t>(S, std::max<int64_t>(1, 192 / items));
     const int forced = env_splits();
     if (forced > 0) S = forced;
     const int64_t max_s = tok_split ? kvq::kMaxSplits - 1 : kvq::kMaxSplits;
